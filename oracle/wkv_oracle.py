@@ -1,0 +1,362 @@
+"""CPU oracle for the WorldKV KV-memory hot path.
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow, obviously correct
+statement of what the GPU library computes, used to prove it right. Only the
+test suite, the smoke check and the benchmark's CPU-baseline leg may import
+it; the product path never does. It shares no code with the HIP library.
+
+Everything is numpy in float64 (bf16 inputs convert to float64 exactly),
+except where a result is an encoding whose precision is fixed by the format
+(the int4 dequantisation product and the bf16 rounding that follows it, and
+the float32 query pose). Library primitives used as steps: ``np.sum`` /
+``np.matmul`` for dot products, ``np.lexsort`` for ordering.
+
+Sources (cited by page title and section):
+
+* "WorldKV: Efficient World Memory with World Retrieval and Compression"
+  (WorldKV): Sec. 4.2 "World Retrieval Mechanism" (top-k retrieval), Sec. 4.3
+  "World Compression Mechanism" (anchor-frame key-key cosine, bottom-P %
+  retention, anchor + retained tokens), Sec. 5.1 "Implementation Details"
+  (window partition sink / retrieval / recent / denoising; pose distance =
+  squared-L2 translation + geodesic rotation, each normalised over the
+  candidate set).
+* "WorldPager" (thelatestinai summary): abstract and Fig. 2 (int4 KV store;
+  retrieval set of the next chunk from the extrapolated camera pose).
+* WorldAttention breakdown (pinghaoyang.com.cn): "from video attention to long
+  interaction" (scaled dot-product attention of the current chunk's queries
+  over the visible keys, 1/sqrt(d) scaling) and the custom-kernel section
+  (online-softmax tiles; the oracle instead uses the direct two-pass form).
+
+Readings where the pages are silent or ambiguous (each is listed with its
+reason in the design notes):
+
+* The compression score compares each non-anchor key with the anchor key at
+  the *same token position*, per head, and averages the cosine over heads
+  (the paper's equation averages over all anchor tokens; the position-aligned
+  head mean is the form the workload definition fixes).
+* The keep ratio r is the fraction of pooled non-anchor tokens retained;
+  n_keep = round-half-away(r * (F-1) * T) computed in float64 from r as a
+  float32, clamped to [0, (F-1)*T].
+* Ties in the score are broken by the lower pooled index p = (f-1)*T + j; a
+  NaN score orders above every number. A zero-norm key has cosine 0.
+* The compressed chunk is the anchor rows in order, then the kept rows in
+  ascending source order.
+* Pose distance: translation term = squared L2; rotation term = |wrap(yaw_i -
+  yaw_q)| with wrap into (-pi, pi]; each term min-max normalised over the
+  candidates (0 when its range is 0); the k smallest (D, index) pairs are
+  returned in ascending chunk index.
+* Query-pose extrapolation: q = last + (last - prev), yaw wrapped.
+* Window order: sink | retrieved chunks in ascending chunk id | recent
+  segments in temporal order | current chunk.
+* int4 store: symmetric groups of 32 along D within one (token, head) row,
+  element d in byte d/2 (low nibble for even d), nibble sign-extended to
+  [-8, 7], value = bf16_RNE(float32(q) * float32(scale)).
+* Attention: no mask, scale 1/sqrt(D) unless given, equal query and key
+  head counts, log-sum-exp in natural log.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TWO_PI = 2.0 * math.pi
+
+
+# ----------------------------------------------------------------------------
+# bf16 encoding
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(b) -> np.ndarray:
+    """bf16 bit patterns (uint16/int16 array) -> float64, exactly."""
+    u = np.asarray(b).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest even (NaN kept quiet)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    r = np.where(nan, ((u >> np.uint64(16)).astype(np.uint16) | np.uint16(0x40)), r)
+    return r.astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# World Compression (WorldKV Sec. 4.3)
+# ----------------------------------------------------------------------------
+
+def keep_count(F: int, T: int, r: float) -> int:
+    """Number of non-anchor tokens kept: round(r * (F-1) * T), clamped.
+
+    WorldKV Sec. 4.3: keep the bottom P % of the pooled non-anchor tokens
+    ("approximately" half of the chunk at P = 25 %, F = 3). r is taken as the
+    float32 the library receives; the product is formed in float64 and rounded
+    half away from zero.
+    """
+    N = (F - 1) * T
+    x = float(np.float32(r)) * N
+    n = int(x)
+    if x - n >= 0.5:
+        n += 1
+    return max(0, min(N, n))
+
+
+def compress_scores(k_bits, F: int, T: int) -> np.ndarray:
+    """Redundancy score of every non-anchor token of one chunk, float64 [(F-1)*T].
+
+    WorldKV Sec. 4.3 (key-key cosine similarity to the anchor frame): for frame
+    f >= 1 and token j, per head h,
+        cos_h = <k[f,j,h], k[0,j,h]> / sqrt(|k[f,j,h]|^2 * |k[0,j,h]|^2)
+    (0 when either norm is 0), and s = (1/H) * sum_h cos_h. The pooled index of
+    (f, j) is p = (f-1)*T + j.
+    """
+    K = bf16_to_f64(k_bits)
+    FT, H, D = K.shape
+    assert FT == F * T
+    K = K.reshape(F, T, H, D)
+    anchor = K[0]
+    na = np.sum(anchor * anchor, axis=-1)                # [T][H]
+    s = np.empty((F - 1, T), dtype=np.float64)
+    for f in range(1, F):
+        kf = K[f]
+        nk = np.sum(kf * kf, axis=-1)                    # [T][H]
+        dt = np.sum(kf * anchor, axis=-1)                # [T][H]
+        prod = nk * na
+        safe = np.where(prod == 0.0, 1.0, prod)
+        with np.errstate(invalid="ignore"):
+            cos = np.where(prod == 0.0, 0.0, dt / np.sqrt(safe))
+        s[f - 1] = np.sum(cos, axis=-1) / H
+    return s.reshape(-1)
+
+
+def select_kept(scores: np.ndarray, n_keep: int) -> np.ndarray:
+    """Pooled indices of the n_keep lowest scores, ascending.
+
+    WorldKV Sec. 4.3: retain the bottom P % of the pooled non-anchor tokens by
+    similarity. Order is lexicographic on (score, pooled index); NaN sorts
+    above every number.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    key = np.where(np.isnan(s), np.inf, s)
+    p = np.arange(s.shape[0])
+    order = np.lexsort((p, key))              # primary: key, secondary: index
+    return np.sort(order[:n_keep])
+
+
+def compress_chunk(k_bits, v_bits, F: int, T: int, r: float):
+    """World Compression of one (chunk, layer) unit.
+
+    WorldKV Sec. 4.3: the compressed chunk is every anchor-frame token plus
+    the retained tokens. Returns (k_out, v_out, kept_idx, scores) with k_out /
+    v_out bf16 bits [T + n_keep][H][D], kept_idx int32 in-chunk source rows
+    (anchor rows 0..T-1 then kept rows ascending) and scores float64
+    [(F-1)*T].
+    """
+    k_bits = np.asarray(k_bits).view(np.uint16)
+    v_bits = np.asarray(v_bits).view(np.uint16)
+    n_keep = keep_count(F, T, r)
+    scores = compress_scores(k_bits, F, T)
+    kept = select_kept(scores, n_keep)
+    kept_idx = np.concatenate([np.arange(T), T + kept]).astype(np.int32)
+    return k_bits[kept_idx], v_bits[kept_idx], kept_idx, scores
+
+
+# ----------------------------------------------------------------------------
+# World Retrieval by camera pose (WorldKV Sec. 4.2, Sec. 5.1; WorldPager Fig. 2)
+# ----------------------------------------------------------------------------
+
+def wrap_angle(a):
+    """Map an angle (float64) into (-pi, pi]: a - 2*pi*rint(a / (2*pi)),
+    then -pi moved to +pi."""
+    a = np.asarray(a, dtype=np.float64)
+    w = a - TWO_PI * np.rint(a / TWO_PI)
+    w = np.where(w <= -math.pi, w + TWO_PI, w)
+    return np.where(w > math.pi, w - TWO_PI, w)
+
+
+def _minmax(v: np.ndarray) -> np.ndarray:
+    lo, hi = v.min(), v.max()
+    if hi == lo:
+        return np.zeros_like(v)
+    return (v - lo) / (hi - lo)
+
+
+def pose_distances(poses, query) -> np.ndarray:
+    """Retrieval distance of every stored chunk to the query pose, float64 [M].
+
+    WorldKV Sec. 5.1 "Implementation Details": squared L2 distance in
+    translation plus geodesic distance in rotation, each normalised across the
+    retrieval candidate set, summed. With a yaw-only rotation the geodesic
+    distance is |wrap(yaw_i - yaw_q)|. Normalisation is min-max.
+    """
+    P = np.asarray(poses, dtype=np.float32).astype(np.float64)
+    q = np.asarray(query, dtype=np.float32).astype(np.float64)
+    dx = P[:, 0] - q[0]
+    dy = P[:, 1] - q[1]
+    dz = P[:, 2] - q[2]
+    dtr = (dx * dx + dy * dy) + dz * dz
+    drot = np.abs(wrap_angle(P[:, 3] - q[3]))
+    return _minmax(dtr) + _minmax(drot)
+
+
+def pose_topk(poses, query, k: int):
+    """R = Top-k by smallest distance (WorldKV Sec. 4.2 retrieval equation,
+    with sim = -distance). Returns (idx ascending int32, distances float64)."""
+    d = pose_distances(poses, query)
+    M = d.shape[0]
+    k_eff = min(k, M)
+    order = np.lexsort((np.arange(M), d))
+    idx = np.sort(order[:k_eff]).astype(np.int32)
+    return idx, d[idx]
+
+
+def pose_extrapolate(prev, last) -> np.ndarray:
+    """Linear pose extrapolation for the next chunk's retrieval (WorldPager
+    Fig. 2: the retrieval set of chunk c+1 is computed from the extrapolated
+    camera pose). q = last + (last - prev) in float64, yaw wrapped, stored as
+    float32."""
+    p = np.asarray(prev, dtype=np.float32).astype(np.float64)
+    l = np.asarray(last, dtype=np.float32).astype(np.float64)
+    q = np.empty(4, dtype=np.float64)
+    q[:3] = 2.0 * l[:3] - p[:3]
+    q[3] = wrap_angle(l[3] + wrap_angle(l[3] - p[3]))
+    return q.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# int4 store (WorldPager abstract, Fig. 2: the KV memory is held as int4)
+# ----------------------------------------------------------------------------
+
+def int4_dequant(packed, scale_bits) -> np.ndarray:
+    """int4 group-quantised rows -> bf16 bit patterns.
+
+    packed: uint8 [..., D/2]; scale_bits: bf16 bits [..., D/32]. Element d
+    is the low nibble of byte d/2 when d is even, the high nibble when odd,
+    read as a signed 4-bit integer q; its value is bf16_RNE(float32(q) *
+    float32(scale[d // 32])).
+    """
+    b = np.asarray(packed, dtype=np.uint8)
+    lo = (b & 0x0F).astype(np.int32)
+    hi = (b >> 4).astype(np.int32)
+    q = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int32)
+    q[..., 0::2] = lo
+    q[..., 1::2] = hi
+    q = np.where(q >= 8, q - 16, q)
+    sc = bf16_to_f64(scale_bits).astype(np.float32)
+    sc = np.repeat(sc, 32, axis=-1)
+    prod = q.astype(np.float32) * sc          # exact: |q| <= 8, scale has 8 bits
+    return f32_to_bf16_rne(prod)
+
+
+def int4_quantize(x_bits):
+    """bf16 rows -> (packed uint8 [..., D/2], scale bf16 bits [..., D/32]).
+
+    Symmetric per-32 group: scale = bf16_RNE(float32(max|x|) / 7 in float32),
+    q = clamp(rint(x / scale in float32), -8, 7), q = 0 when the scale is 0.
+    (Harness-side encoder used to build test banks; not on the hot path.)
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    shp = x.shape
+    D = shp[-1]
+    g = x.reshape(shp[:-1] + (D // 32, 32))
+    amax = np.max(np.abs(g), axis=-1)
+    sbits = f32_to_bf16_rne(amax / np.float32(7.0))
+    s = bf16_to_f64(sbits).astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s == 0, 0.0, np.rint(g / np.where(s == 0, 1, s)))
+    q = np.clip(q, -8, 7).astype(np.int32).reshape(shp)
+    u = (q & 0x0F).astype(np.uint8)
+    packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+    return packed, sbits
+
+
+# ----------------------------------------------------------------------------
+# Window assembly (WorldKV Sec. 4.2 / 5.1; WorldAttention contiguous copy)
+# ----------------------------------------------------------------------------
+
+def window_offsets(n_sink: int, n_ret: int, Lc: int, recent_lens, n_cur: int):
+    """Row offsets of the four window regions: (off_ret, off_rec, off_cur, Nk)."""
+    off_ret = n_sink
+    off_rec = off_ret + n_ret * Lc
+    off_cur = off_rec + int(sum(recent_lens))
+    return off_ret, off_rec, off_cur, off_cur + n_cur
+
+
+def assemble_window(sink, bank, idx, recent, current):
+    """Attention window rows in the order sink | retrieved | recent | current.
+
+    WorldKV Sec. 4.2: retrieved chunks are inserted back into the native
+    attention window without re-encoding; Sec. 5.1 gives the partition sink /
+    retrieval / recent / denoising. Each argument is a (k, v) pair of bf16
+    bit arrays [n][H][D]; ``bank`` is (k, v) [M][Lc][H][D]; ``idx`` are the
+    retrieved chunk ids (ascending). Returns (win_k, win_v).
+    """
+    parts_k = [np.asarray(sink[0]).view(np.uint16)]
+    parts_v = [np.asarray(sink[1]).view(np.uint16)]
+    bk = np.asarray(bank[0]).view(np.uint16)
+    bv = np.asarray(bank[1]).view(np.uint16)
+    for i in idx:
+        parts_k.append(bk[int(i)])
+        parts_v.append(bv[int(i)])
+    for k, v in recent:
+        parts_k.append(np.asarray(k).view(np.uint16))
+        parts_v.append(np.asarray(v).view(np.uint16))
+    parts_k.append(np.asarray(current[0]).view(np.uint16))
+    parts_v.append(np.asarray(current[1]).view(np.uint16))
+    return np.concatenate(parts_k, axis=0), np.concatenate(parts_v, axis=0)
+
+
+def dequant_bank_chunks(packed_k, packed_v, scale_k, scale_v, idx):
+    """bf16 bit rows of the listed int4 bank chunks: (k [n][Lc][H][D], v ...)."""
+    ks = [int4_dequant(packed_k[int(i)], scale_k[int(i)]) for i in idx]
+    vs = [int4_dequant(packed_v[int(i)], scale_v[int(i)]) for i in idx]
+    return np.stack(ks), np.stack(vs)
+
+
+# ----------------------------------------------------------------------------
+# Chunk attention (WorldAttention: scaled dot-product attention of the current
+# chunk's queries over the visible history; WorldKV Sec. 1 / 5.2: attention of
+# the denoising chunk over the window)
+# ----------------------------------------------------------------------------
+
+def chunk_attention(q_bits, k_bits, v_bits, scale: float | None = None):
+    """O[i,h] = sum_j softmax_j(scale * <Q[i,h], K[j,h]>) V[j,h], no mask.
+
+    Direct two-pass form in float64: s = scale * Q K^T per head, m = row max,
+    w = exp(s - m), l = sum w, O = (w V) / l, LSE = m + ln l.
+    Returns (O float64 [Nq][H][D], LSE float64 [H][Nq]).
+    """
+    Q = bf16_to_f64(q_bits)
+    K = bf16_to_f64(k_bits)
+    V = bf16_to_f64(v_bits)
+    Nq, H, D = Q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    O = np.empty((Nq, H, D), dtype=np.float64)
+    LSE = np.empty((H, Nq), dtype=np.float64)
+    for h in range(H):
+        s = scale * np.matmul(Q[:, h, :], K[:, h, :].T)      # [Nq][Nk]
+        m = np.max(s, axis=1, keepdims=True)
+        w = np.exp(s - m)
+        l = np.sum(w, axis=1, keepdims=True)
+        O[:, h, :] = np.matmul(w, V[:, h, :]) / l
+        LSE[h] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def attention_weights(q_bits, k_bits, scale: float | None = None) -> np.ndarray:
+    """Normalised attention weights [H][Nq][Nk] (used by invariant checks)."""
+    Q = bf16_to_f64(q_bits)
+    K = bf16_to_f64(k_bits)
+    Nq, H, D = Q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    out = []
+    for h in range(H):
+        s = scale * np.matmul(Q[:, h, :], K[:, h, :].T)
+        w = np.exp(s - np.max(s, axis=1, keepdims=True))
+        out.append(w / np.sum(w, axis=1, keepdims=True))
+    return np.stack(out)

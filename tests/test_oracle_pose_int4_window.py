@@ -1,0 +1,178 @@
+"""Pins for the oracle's pose retrieval (WorldKV Sec. 4.2 / 5.1), query-pose
+extrapolation (WorldPager Fig. 2), int4 store (WorldPager abstract) and
+window assembly (WorldKV Sec. 4.2 / 5.1)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wkv_oracle as O
+
+
+# ---------------------------------------------------------------- pose top-k
+
+def test_pose_worked_example_by_hand():
+    # Distances derived by hand from the recipe of WorldKV Sec. 5.1 (squared L2
+    # translation + |yaw difference|, each min-max normalised):
+    #   translation^2 = [1, 2, 4]      -> normalised [0, 1/3, 1]
+    #   rotation      = [.5, .25, .125] -> normalised [1, 1/3, 0]
+    #   distance      = [1, 2/3, 1]; the tie 1 = 1 goes to the lower index.
+    q = [0.0, 0.0, 0.0, 0.0]
+    P = [[1, 0, 0, 0.5], [1, 1, 0, 0.25], [0, 2, 0, -0.125]]
+    d = O.pose_distances(P, q)
+    assert d[0] == 1.0 and d[2] == 1.0
+    assert abs(d[1] - 2.0 / 3.0) < 1e-15
+    assert list(O.pose_topk(P, q, 1)[0]) == [1]
+    assert list(O.pose_topk(P, q, 2)[0]) == [0, 1]
+    assert list(O.pose_topk(P, q, 3)[0]) == [0, 1, 2]
+    assert list(O.pose_topk(P, q, 7)[0]) == [0, 1, 2]
+
+
+def test_yaw_wraps_around():
+    # yaw 3.0 vs -3.0 are 2*pi - 6 apart, not 6.
+    P = [[0, 0, 0, 3.0], [0, 0, 0, 1.0], [0, 0, 0, -3.0]]
+    q = [0, 0, 0, -3.0]
+    w = O.wrap_angle(np.float64(np.float32(3.0)) - np.float64(np.float32(-3.0)))
+    assert abs(abs(w) - (2 * math.pi - 6.0)) < 1e-15
+    idx, _ = O.pose_topk(P, q, 2)
+    assert list(idx) == [0, 2]
+    assert O.wrap_angle(math.pi) == math.pi
+    assert O.wrap_angle(-math.pi) == math.pi
+    assert abs(O.wrap_angle(3 * math.pi / 2) + math.pi / 2) < 1e-15
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_pose_topk_against_full_sort_and_invariances(seed):
+    rng = np.random.default_rng(seed)
+    M = 40
+    # dyadic grid so that shifted / scaled copies stay exact in float32
+    P = np.round(rng.uniform(-8, 8, (M, 4)) * 8) / 8
+    P[:, 3] = np.round(rng.uniform(-1, 1, M) * 8) / 8
+    q = np.array([0.5, -0.25, 1.0, 0.125])
+    d = O.pose_distances(P, q)
+    for k in (1, 3, 10, M, M + 5):
+        idx, dist = O.pose_topk(P, q, k)
+        full = sorted(range(M), key=lambda i: (d[i], i))[: min(k, M)]
+        assert list(idx) == sorted(full)
+        assert np.array_equal(dist, d[idx])
+    base = O.pose_topk(P, q, 5)[0]
+    Pt, qt = P.copy(), q.copy()
+    Pt[:, :3] += 3.0
+    qt[:3] += 3.0
+    assert np.array_equal(O.pose_topk(Pt, qt, 5)[0], base)
+    Ps, qs = P.copy(), q.copy()
+    Ps[:, :3] *= 2.0
+    qs[:3] *= 2.0
+    assert np.array_equal(O.pose_distances(Ps, qs), d)
+    Py, qy = P.copy(), q.copy()
+    Py[:, 3] += 0.5
+    qy[3] += 0.5
+    assert np.array_equal(O.pose_distances(Py, qy), d)
+
+
+def test_pose_degenerate_ranges():
+    P = [[1, 1, 1, 0.5]] * 4
+    d = O.pose_distances(P, [0, 0, 0, 0])
+    assert np.all(d == 0.0)
+    assert list(O.pose_topk(P, [0, 0, 0, 0], 2)[0]) == [0, 1]
+
+
+def test_pose_extrapolation():
+    q = O.pose_extrapolate([0, 0, 0, 0.1], [1, 2, 3, 0.3])
+    assert q.dtype == np.float32
+    assert list(q[:3]) == [2.0, 4.0, 6.0]
+    assert abs(float(q[3]) - 0.5) < 1e-6
+    # crossing the +-pi seam: from 3.0 to -3.0 is a +0.2832 turn
+    q = O.pose_extrapolate([0, 0, 0, 3.0], [0, 0, 0, -3.0])
+    step = 2 * math.pi - 6.0
+    assert abs(float(q[3]) - (-3.0 + step)) < 1e-6
+
+
+# ---------------------------------------------------------------- int4 store
+
+def _pack(qvals):
+    q = np.asarray(qvals, dtype=np.int32) & 0xF
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def test_int4_all_nibbles_closed_form():
+    qv = np.array([i - 8 for i in range(16)] * 2, dtype=np.int32)   # 32 values
+    packed = _pack(qv)[None]
+    for scale, expect in [
+        (1.0, qv.astype(np.float64)),
+        (0.25, qv / 4.0),
+        (2.0 ** -6, qv / 64.0),
+    ]:
+        sb = O.f32_to_bf16_rne(np.array([[scale]], dtype=np.float32))
+        out = O.bf16_to_f64(O.int4_dequant(packed, sb))[0]
+        assert np.array_equal(out, expect)
+    # scale 1 + 2^-7: q * scale needs 11 bits and is rounded to bf16 by hand:
+    #   7 * 1.0078125 = 7.0546875 = 1.11000011 1 x 2^2 -> 7.0625 (round up)
+    #  -3 * 1.0078125 = -3.0234375 = -1.1000001 1 x 2^1 -> -3.03125 (tie -> even)
+    sb = O.f32_to_bf16_rne(np.array([[1.0078125]], dtype=np.float32))
+    out = O.bf16_to_f64(O.int4_dequant(packed, sb))[0]
+    assert out[15] == 7.0625
+    assert out[5] == -3.03125
+    assert out[9] == 1.0078125
+    assert out[8] == 0.0
+
+
+def test_int4_nibble_order_low_is_even():
+    packed = np.array([[0x21] + [0] * 15], dtype=np.uint8)     # d0 = 1, d1 = 2
+    sb = O.f32_to_bf16_rne(np.array([[1.0]], dtype=np.float32))
+    out = O.bf16_to_f64(O.int4_dequant(packed, sb))[0]
+    assert out[0] == 1.0 and out[1] == 2.0 and np.all(out[2:] == 0)
+
+
+def test_int4_roundtrip_and_error_bound():
+    rng = np.random.default_rng(3)
+    qv = rng.integers(-7, 8, (5, 3, 64))
+    qv[..., 0] = 7
+    qv[..., 32] = -7                            # every group's max|x| is 7
+    xb = O.f32_to_bf16_rne(qv.astype(np.float32))
+    packed, sb = O.int4_quantize(xb)
+    assert np.all(O.bf16_to_f64(sb) == 1.0)
+    assert np.array_equal(O.int4_dequant(packed, sb), xb)
+    x = rng.standard_normal((50, 2, 128)).astype(np.float32)
+    xb = O.f32_to_bf16_rne(x)
+    packed, sb = O.int4_quantize(xb)
+    xr = O.bf16_to_f64(O.int4_dequant(packed, sb))
+    xs = O.bf16_to_f64(xb)
+    s = np.repeat(O.bf16_to_f64(sb), 32, axis=-1)
+    assert np.all(np.abs(xr - xs) <= 0.5 * s * (1 + 2 ** -7) + np.abs(xr) * 2 ** -8 + 1e-30)
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0,
+                                  3.4e38, 1e-40], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16_rne(x), ref)
+
+
+# ---------------------------------------------------------------- window
+
+def test_window_layout_and_offsets():
+    rng = np.random.default_rng(5)
+    H, D, Lc, M = 2, 64, 6, 5
+
+    def seg(n):
+        return (rng.integers(0, 65535, (n, H, D), dtype=np.uint16),
+                rng.integers(0, 65535, (n, H, D), dtype=np.uint16))
+
+    sink = seg(4)
+    bank = (rng.integers(0, 65535, (M, Lc, H, D), dtype=np.uint16),
+            rng.integers(0, 65535, (M, Lc, H, D), dtype=np.uint16))
+    recent = [seg(3), seg(5)]
+    cur = seg(7)
+    idx = [1, 4]
+    wk, wv = O.assemble_window(sink, bank, idx, recent, cur)
+    off_ret, off_rec, off_cur, Nk = O.window_offsets(4, 2, Lc, [3, 5], 7)
+    assert (off_ret, off_rec, off_cur, Nk) == (4, 16, 24, 31)
+    assert wk.shape == (Nk, H, D)
+    assert np.array_equal(wk[:4], sink[0])
+    assert np.array_equal(wk[4:10], bank[0][1]) and np.array_equal(wv[10:16], bank[1][4])
+    assert np.array_equal(wk[16:19], recent[0][0]) and np.array_equal(wv[19:24], recent[1][1])
+    assert np.array_equal(wv[24:], cur[1])
