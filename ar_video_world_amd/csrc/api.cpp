@@ -1,0 +1,264 @@
+// C ABI of libwkv: argument validation on the host (before anything is
+// enqueued), workspace sizing and launch planning. The operations themselves
+// are defined in include/wkv.h and run in the kernel translation units.
+#include "../../include/wkv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "wkv_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wkv_status fail(wkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+wkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(WKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wkv_status check_hd(int32_t H, int32_t D) {
+  if (D != 64 && D != 128) return fail(WKV_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
+  if (H < 1 || (int64_t)H * D > 8192) return fail(WKV_ERR_SHAPE, "heads H=%d out of range (1..%d)", H, 8192 / D);
+  return WKV_OK;
+}
+
+// Compute units of the current device, cached per device id.
+int num_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int64_t keep_count(int32_t F, int32_t T, float r) {
+  const int64_t N = (int64_t)(F - 1) * T;
+  const double x = (double)r * (double)N;
+  int64_t n = (int64_t)x;
+  if (x - (double)n >= 0.5) ++n;
+  if (n < 0) n = 0;
+  if (n > N) n = N;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wkv_abi_version(void) { return WKV_ABI_VERSION; }
+
+const char* wkv_last_error(void) { return g_err; }
+
+int32_t wkv_keep_count(int32_t F, int32_t T, float r) {
+  if (F < 2 || T < 1 || !(r >= 0.0f && r <= 1.0f)) return -1;
+  if ((int64_t)(F - 1) * T > (int64_t)INT32_MAX) return -1;
+  return (int32_t)keep_count(F, T, r);
+}
+
+size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T) {
+  if (B < 1 || F < 2 || T < 1) return 0;
+  return (size_t)B * (size_t)(F - 1) * (size_t)T * sizeof(double);
+}
+
+wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
+                              int32_t T, int32_t H, int32_t D, float r, uint16_t* k_out,
+                              uint16_t* v_out, int32_t* kept_idx, double* scores, void* ws,
+                              size_t ws_bytes, wkv_stream_t stream) {
+  if (!k || !v || !k_out || !v_out || !kept_idx)
+    return fail(WKV_ERR_NULL, "wkv_compress_chunk: k, v, k_out, v_out and kept_idx are required");
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (B < 1 || F < 2 || F > 4 || T < 1)
+    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: need B>=1, 2<=F<=4, T>=1 (B=%d F=%d T=%d)", B, F, T);
+  if ((int64_t)(F - 1) * T > 8192)
+    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: (F-1)*T=%lld exceeds 8192",
+                (long long)(F - 1) * T);
+  if ((int64_t)B * F * T * H * D >= ((int64_t)1 << 40))
+    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: batch too large");
+  if (!(r >= 0.0f && r <= 1.0f)) return fail(WKV_ERR_RATIO, "wkv_compress_chunk: r=%g not in [0,1]", (double)r);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out) ||
+      !aligned16(kept_idx) || (scores && !aligned16(scores)) || (ws && !aligned16(ws)))
+    return fail(WKV_ERR_ALIGN, "wkv_compress_chunk: device pointers must be 16-byte aligned");
+  const int n_keep = (int)keep_count(F, T, r);
+  const int N = (F - 1) * T;
+  const bool need_scores = scores != nullptr;
+  const bool score = need_scores || (n_keep > 0 && n_keep < N);
+  double* sbuf = scores;
+  if (score && !sbuf) {
+    const size_t need = wkv_compress_workspace_bytes(B, F, T);
+    if (!ws || ws_bytes < need)
+      return fail(WKV_ERR_WORKSPACE, "wkv_compress_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
+    sbuf = static_cast<double*>(ws);
+  }
+  hipError_t e = wkv::compress_launch(k, v, B, F, T, H, D, n_keep, k_out, v_out, kept_idx, sbuf,
+                                      need_scores, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_compress_chunk launch");
+  return WKV_OK;
+}
+
+wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M, const wkv_pose* query_hist,
+                         int32_t n_hist, int32_t k, int32_t* out_idx, double* out_dist,
+                         wkv_pose* out_query, wkv_stream_t stream) {
+  if (!bank_poses || !query_hist || !out_idx)
+    return fail(WKV_ERR_NULL, "wkv_pose_topk: bank_poses, query_hist and out_idx are required");
+  if (M < 1 || M > 8192) return fail(WKV_ERR_SHAPE, "wkv_pose_topk: M=%d not in [1, 8192]", M);
+  if (k < 1) return fail(WKV_ERR_K, "wkv_pose_topk: k=%d < 1", k);
+  if (n_hist != 1 && n_hist != 2) return fail(WKV_ERR_K, "wkv_pose_topk: n_hist=%d (must be 1 or 2)", n_hist);
+  if (!aligned16(bank_poses) || !aligned16(out_idx) || (out_dist && !aligned16(out_dist)) ||
+      (out_query && !aligned16(out_query)))
+    return fail(WKV_ERR_ALIGN, "wkv_pose_topk: device pointers must be 16-byte aligned");
+  const float* last = &query_hist[n_hist - 1].x;
+  const float* prev = n_hist == 2 ? &query_hist[0].x : nullptr;
+  const int k_eff = k < M ? k : M;
+  hipError_t e = wkv::pose_topk_launch(bank_poses, M, last, prev, n_hist, k_eff, out_idx,
+                                       out_dist, out_query, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_pose_topk launch");
+  return WKV_OK;
+}
+
+wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,
+                               const int32_t* retrieved_idx, int32_t n_ret,
+                               const wkv_segment* recent, int32_t n_recent,
+                               const wkv_segment* current, int32_t H, int32_t D,
+                               uint16_t* win_k, uint16_t* win_v, int64_t win_rows,
+                               wkv_stream_t stream) {
+  if (!sink || !current || !win_k || !win_v)
+    return fail(WKV_ERR_NULL, "wkv_assemble_window: sink, current, win_k and win_v are required");
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (n_ret < 0 || n_recent < 0 || n_recent > wkv::kMaxSegments - 2)
+    return fail(WKV_ERR_SHAPE, "wkv_assemble_window: n_ret=%d n_recent=%d (0..%d)", n_ret, n_recent,
+                wkv::kMaxSegments - 2);
+  if (n_ret > 0 && (!bank || !retrieved_idx))
+    return fail(WKV_ERR_NULL, "wkv_assemble_window: n_ret>0 needs bank and retrieved_idx");
+  if (n_recent > 0 && !recent) return fail(WKV_ERR_NULL, "wkv_assemble_window: recent is NULL");
+  if (!aligned16(win_k) || !aligned16(win_v) || (retrieved_idx && !aligned16(retrieved_idx)))
+    return fail(WKV_ERR_ALIGN, "wkv_assemble_window: device pointers must be 16-byte aligned");
+
+  wkv::AssemblePlan p;
+  std::memset(&p, 0, sizeof(p));
+  // Segments: sink, recent..., current, in window order.
+  const wkv_segment* segs[wkv::kMaxSegments];
+  int ns = 0;
+  segs[ns++] = sink;
+  for (int i = 0; i < n_recent; ++i) segs[ns++] = &recent[i];
+  segs[ns++] = current;
+  for (int i = 0; i < ns; ++i) {
+    const wkv_segment* s = segs[i];
+    if (s->n < 0) return fail(WKV_ERR_SHAPE, "wkv_assemble_window: segment %d has n=%d", i, s->n);
+    if (s->n > 0 && (!s->k || !s->v))
+      return fail(WKV_ERR_NULL, "wkv_assemble_window: segment %d has n=%d but NULL k/v", i, s->n);
+    if (!aligned16(s->k) || !aligned16(s->v))
+      return fail(WKV_ERR_ALIGN, "wkv_assemble_window: segment %d pointers must be 16-byte aligned", i);
+  }
+  int Lc = 0, M = 0, int4 = 0;
+  if (n_ret > 0) {
+    if (bank->dtype != WKV_BANK_BF16 && bank->dtype != WKV_BANK_INT4_G32)
+      return fail(WKV_ERR_UNSUPPORTED, "wkv_assemble_window: bank dtype %d", bank->dtype);
+    if (bank->M < 1 || bank->Lc < 1)
+      return fail(WKV_ERR_SHAPE, "wkv_assemble_window: bank M=%d Lc=%d", bank->M, bank->Lc);
+    if (!bank->k || !bank->v) return fail(WKV_ERR_NULL, "wkv_assemble_window: bank k/v NULL");
+    int4 = bank->dtype == WKV_BANK_INT4_G32;
+    if (int4 && (!bank->k_scale || !bank->v_scale))
+      return fail(WKV_ERR_NULL, "wkv_assemble_window: int4 bank needs k_scale and v_scale");
+    if (!aligned16(bank->k) || !aligned16(bank->v) ||
+        (int4 && (!aligned16(bank->k_scale) || !aligned16(bank->v_scale))))
+      return fail(WKV_ERR_ALIGN, "wkv_assemble_window: bank pointers must be 16-byte aligned");
+    Lc = bank->Lc;
+    M = bank->M;
+  }
+  int64_t row = 0;
+  p.seg_start[0] = 0;
+  p.seg_k[0] = sink->k;
+  p.seg_v[0] = sink->v;
+  row = sink->n;
+  p.ret_off = row;
+  row += (int64_t)n_ret * Lc;
+  for (int i = 1; i < ns; ++i) {
+    p.seg_start[i] = row;
+    p.seg_k[i] = segs[i]->k;
+    p.seg_v[i] = segs[i]->v;
+    row += segs[i]->n;
+  }
+  p.seg_start[ns] = row;
+  p.nseg = ns;
+  p.Nk = row;
+  if (p.Nk > win_rows)
+    return fail(WKV_ERR_SHAPE, "wkv_assemble_window: window needs %lld rows, capacity %lld",
+                (long long)p.Nk, (long long)win_rows);
+  if (p.Nk == 0) return WKV_OK;
+  p.bank_k = n_ret ? bank->k : nullptr;
+  p.bank_v = n_ret ? bank->v : nullptr;
+  p.bank_ks = n_ret ? bank->k_scale : nullptr;
+  p.bank_vs = n_ret ? bank->v_scale : nullptr;
+  p.idx = retrieved_idx;
+  p.M = M;
+  p.Lc = Lc;
+  p.n_ret = n_ret;
+  p.int4 = int4;
+  p.cpr = H * D / 8;
+  hipError_t e = wkv::assemble_launch(p, win_k, win_v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_assemble_window launch");
+  return WKV_OK;
+}
+
+size_t wkv_attention_workspace_bytes(int32_t Nq, int32_t Nk, int32_t H, int32_t D) {
+  if (Nq < 1 || Nk < 1 || H < 1 || (D != 64 && D != 128)) return 0;
+  wkv::AttnPlan p = wkv::attention_plan(Nq, Nk, H, D, num_cus());
+  return wkv::attention_ws_bytes(p, Nq, H, D);
+}
+
+wkv_status wkv_chunk_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               int32_t Nq, int32_t Nk, int32_t H, int32_t D, float scale,
+                               uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                               wkv_stream_t stream) {
+  if (!q || !k || !v || !out) return fail(WKV_ERR_NULL, "wkv_chunk_attention: q, k, v and out are required");
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (Nq < 1 || Nk < 1) return fail(WKV_ERR_SHAPE, "wkv_chunk_attention: Nq=%d Nk=%d", Nq, Nk);
+  if ((int64_t)Nk * H * D >= ((int64_t)1 << 31) || (int64_t)Nq * H * D >= ((int64_t)1 << 31))
+    return fail(WKV_ERR_SHAPE, "wkv_chunk_attention: Nq*H*D and Nk*H*D must be < 2^31");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (lse && !aligned16(lse)) || (ws && !aligned16(ws)))
+    return fail(WKV_ERR_ALIGN, "wkv_chunk_attention: device pointers must be 16-byte aligned");
+  if (!(scale == scale) || std::isinf(scale))
+    return fail(WKV_ERR_SHAPE, "wkv_chunk_attention: scale is not finite");
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  wkv::AttnPlan plan = wkv::attention_plan(Nq, Nk, H, D, num_cus());
+  // Fewer splits when the workspace is short.
+  while (plan.splits > 1 && (!ws || wkv::attention_ws_bytes(plan, Nq, H, D) > ws_bytes)) {
+    const int kblocks = (Nk + 63) / 64;
+    const int want = plan.splits / 2;
+    const int kb_per = (kblocks + want - 1) / want;
+    plan.keys_per_split = kb_per * 64;
+    plan.splits = (kblocks + kb_per - 1) / kb_per;
+  }
+  if (plan.splits <= 1) {
+    plan.splits = 1;
+    plan.keys_per_split = Nk;
+  }
+  hipError_t e = wkv::attention_launch(q, k, v, Nq, Nk, H, D, sc, out, lse, plan, ws,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_chunk_attention launch");
+  return WKV_OK;
+}
+
+}  // extern "C"

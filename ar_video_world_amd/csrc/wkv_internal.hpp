@@ -1,0 +1,55 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the
+// kernel translation units. Not installed; no torch types anywhere.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr int kMaxSegments = 16;  // sink + up to 14 recent + current
+
+// ---- compression
+int compress_score_tile(int B, int T, int H);
+hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, int T,
+                           int H, int D, int n_keep, uint16_t* k_out, uint16_t* v_out,
+                           int32_t* kept_idx, double* scores, bool need_scores,
+                           hipStream_t s);
+
+// ---- pose top-k
+hipError_t pose_topk_launch(const void* poses, int M, const float* last,
+                            const float* prev, int n_hist, int k_eff, int32_t* out_idx,
+                            double* out_dist, void* out_query, hipStream_t s);
+
+// ---- window assembly
+struct AssemblePlan {
+  const uint16_t* seg_k[kMaxSegments];
+  const uint16_t* seg_v[kMaxSegments];
+  int64_t seg_start[kMaxSegments + 1];
+  int nseg;
+  const void* bank_k;
+  const void* bank_v;
+  const uint16_t* bank_ks;
+  const uint16_t* bank_vs;
+  const int32_t* idx;
+  int M, Lc, n_ret, int4;
+  int64_t ret_off;
+  int64_t Nk;
+  int cpr;  // 16-byte chunks per bf16 output row (H*D/8)
+};
+hipError_t assemble_launch(const AssemblePlan& p, uint16_t* win_k, uint16_t* win_v,
+                           hipStream_t s);
+
+// ---- chunk attention
+struct AttnPlan {
+  int splits;       // key splits (1 = write O directly)
+  int keys_per_split;
+};
+AttnPlan attention_plan(int Nq, int Nk, int H, int D, int num_cus);
+size_t attention_ws_bytes(const AttnPlan& p, int Nq, int H, int D);
+hipError_t attention_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            int Nq, int Nk, int H, int D, float scale, uint16_t* out,
+                            float* lse, const AttnPlan& plan, void* ws, hipStream_t s);
+
+}  // namespace wkv

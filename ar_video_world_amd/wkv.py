@@ -1,0 +1,259 @@
+"""Python binding of libwkv (ctypes over the C ABI in include/wkv.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory, data pointers and the current stream. The
+functions carry the C names; outputs not passed in are allocated with torch on
+the inputs' device. Every call raises ``WkvError`` on a non-OK status, and
+importing this module raises when the shared library is missing (there is no
+fallback path).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libwkv.so not found at {LIB_PATH}: build it with "
+        "`python -m ar_video_world_amd.build` (hipcc, gfx950)")
+
+_lib = C.CDLL(LIB_PATH)
+
+WKV_OK = 0
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_RATIO", 4: "ERR_K",
+          5: "ERR_ALIGN", 6: "ERR_WORKSPACE", 7: "ERR_UNSUPPORTED", 8: "ERR_HIP"}
+WKV_BANK_BF16 = 0
+WKV_BANK_INT4_G32 = 1
+
+
+class WkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+class wkv_pose(C.Structure):
+    _fields_ = [("x", C.c_float), ("y", C.c_float), ("z", C.c_float), ("yaw", C.c_float)]
+
+
+class wkv_segment(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n", C.c_int32)]
+
+
+class wkv_bank(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("M", C.c_int32), ("Lc", C.c_int32),
+                ("k", C.c_void_p), ("v", C.c_void_p),
+                ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
+
+
+_P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_abi_version = _sig("wkv_abi_version", _I32, [])
+_last_error = _sig("wkv_last_error", C.c_char_p, [])
+_keep_count = _sig("wkv_keep_count", _I32, [_I32, _I32, _F])
+_compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32, _I32, _I32])
+_compress = _sig("wkv_compress_chunk", C.c_int,
+                 [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P])
+_pose_topk = _sig("wkv_pose_topk", C.c_int,
+                  [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P, _P, _P])
+_assemble = _sig("wkv_assemble_window", C.c_int,
+                 [C.POINTER(wkv_segment), C.POINTER(wkv_bank), _P, _I32,
+                  C.POINTER(wkv_segment), _I32, C.POINTER(wkv_segment), _I32, _I32,
+                  _P, _P, _I64, _P])
+_attn_ws = _sig("wkv_attention_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
+_attn = _sig("wkv_chunk_attention", C.c_int,
+             [_P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P])
+
+EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
+           "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_pose_topk",
+           "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
+
+
+def _check(fn: str, st: int):
+    if st != WKV_OK:
+        raise WkvError(fn, st, wkv_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        if not torch.cuda.is_available():
+            return C.c_void_p(None)
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _bits(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bf16 (or its int16 bits), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def wkv_abi_version() -> int:
+    return int(_abi_version())
+
+
+def wkv_last_error() -> str:
+    s = _last_error()
+    return s.decode() if s else ""
+
+
+def wkv_keep_count(F: int, T: int, r: float) -> int:
+    return int(_keep_count(F, T, r))
+
+
+def wkv_compress_workspace_bytes(B: int, F: int, T: int) -> int:
+    return int(_compress_ws(B, F, T))
+
+
+def wkv_attention_workspace_bytes(Nq: int, Nk: int, H: int, D: int) -> int:
+    return int(_attn_ws(Nq, Nk, H, D))
+
+
+def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
+                       k_out=None, v_out=None, kept_idx=None, scores=None,
+                       want_scores: bool = False, ws=None, stream=None):
+    """World Compression of B units. k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]).
+    Returns (k_out, v_out, kept_idx, scores-or-None)."""
+    _bits(k, "k"), _bits(v, "v")
+    squeeze = k.dim() == 3
+    if squeeze:
+        k, v = k.unsqueeze(0), v.unsqueeze(0)
+    B, FT, H, D = k.shape
+    if FT != F * T:
+        raise ValueError(f"k has {FT} rows per unit, expected F*T={F * T}")
+    n_keep = wkv_keep_count(F, T, r)
+    Lc = T + max(n_keep, 0)
+    dev = k.device
+    if k_out is None:
+        k_out = torch.empty((B, Lc, H, D), dtype=k.dtype, device=dev)
+    if v_out is None:
+        v_out = torch.empty((B, Lc, H, D), dtype=v.dtype, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, Lc), dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((B, (F - 1) * T), dtype=torch.float64, device=dev)
+    if ws is None:
+        nb = wkv_compress_workspace_bytes(B, F, T)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    st = _compress(_ptr(k), _ptr(v), B, F, T, H, D, r, _ptr(k_out), _ptr(v_out),
+                   _ptr(kept_idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
+    _check("wkv_compress_chunk", st)
+    if squeeze:
+        k_out, v_out, kept_idx = k_out[0], v_out[0], kept_idx[0]
+        scores = None if scores is None else scores[0]
+    return k_out, v_out, kept_idx, scores
+
+
+def _pose_tuple(p) -> wkv_pose:
+    x, y, z, yaw = (float(t) for t in p)
+    return wkv_pose(x, y, z, yaw)
+
+
+def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
+                  want_dist: bool = True, want_query: bool = False, stream=None):
+    """Top-k stored chunks by camera-pose distance. bank_poses: float32 [M, 4]
+    on the device. query_hist: one pose (x, y, z, yaw) or [prev, last].
+    Returns (idx int32 [k_eff], dist float64 [k_eff] or None, query or None)."""
+    if bank_poses.dtype != torch.float32 or bank_poses.dim() != 2 or bank_poses.shape[1] != 4:
+        raise TypeError("bank_poses: expected float32 [M, 4]")
+    bank_poses = bank_poses.contiguous()
+    M = bank_poses.shape[0]
+    hist = list(query_hist)
+    if len(hist) == 4 and not hasattr(hist[0], "__len__"):
+        hist = [hist]
+    n_hist = len(hist)
+    arr = (wkv_pose * max(n_hist, 1))(*[_pose_tuple(p) for p in hist])
+    k_eff = min(int(k), M) if k >= 1 else 1
+    dev = bank_poses.device
+    idx = torch.empty(max(k_eff, 1), dtype=torch.int32, device=dev)
+    dist = torch.empty(max(k_eff, 1), dtype=torch.float64, device=dev) if want_dist else None
+    q = torch.empty(4, dtype=torch.float32, device=dev) if want_query else None
+    st = _pose_topk(_ptr(bank_poses), M, arr, n_hist, int(k), _ptr(idx), _ptr(dist),
+                    _ptr(q), _stream(stream))
+    _check("wkv_pose_topk", st)
+    return idx, dist, q
+
+
+def _seg(pair) -> wkv_segment:
+    if pair is None:
+        return wkv_segment(None, None, 0)
+    k, v = pair
+    _bits(k, "segment k"), _bits(v, "segment v")
+    return wkv_segment(k.data_ptr(), v.data_ptr(), int(k.shape[0]))
+
+
+def wkv_assemble_window(sink, bank, retrieved_idx: Optional[torch.Tensor], recent, current,
+                        H: int, D: int, win_k=None, win_v=None, stream=None):
+    """Window rows sink | retrieved | recent | current.
+
+    sink, current: (k, v) bf16 [n, H, D]. recent: list of (k, v).
+    bank: dict with 'k', 'v' (bf16 [M, Lc, H, D], or uint8 [M, Lc, H, D/2] with
+    'k_scale', 'v_scale' bf16 [M, Lc, H, D/32] for the int4 store), or None.
+    Returns (win_k, win_v)."""
+    sk = _seg(sink)
+    cur = _seg(current)
+    rec_list = list(recent or [])
+    rec = (wkv_segment * max(len(rec_list), 1))(*[_seg(p) for p in rec_list])
+    n_ret = 0 if retrieved_idx is None else int(retrieved_idx.numel())
+    bk = wkv_bank(0, 0, 0, None, None, None, None)
+    if bank is not None and n_ret > 0:
+        int4 = "k_scale" in bank and bank["k_scale"] is not None
+        bk.dtype = WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16
+        bk.M, bk.Lc = int(bank["k"].shape[0]), int(bank["k"].shape[1])
+        bk.k, bk.v = bank["k"].data_ptr(), bank["v"].data_ptr()
+        if int4:
+            bk.k_scale, bk.v_scale = bank["k_scale"].data_ptr(), bank["v_scale"].data_ptr()
+    Lc = bk.Lc if n_ret > 0 else 0
+    Nk = sk.n + n_ret * Lc + sum(int(p[0].shape[0]) for p in rec_list) + cur.n
+    dev = (sink[0] if sink is not None else current[0]).device
+    if win_k is None:
+        win_k = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev)
+    if win_v is None:
+        win_v = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev)
+    st = _assemble(C.byref(sk), C.byref(bk), _ptr(retrieved_idx), n_ret, rec, len(rec_list),
+                   C.byref(cur), H, D, _ptr(win_k), _ptr(win_v), int(win_k.shape[0]),
+                   _stream(stream))
+    _check("wkv_assemble_window", st)
+    return win_k, win_v
+
+
+def wkv_chunk_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        scale: float = 0.0, out=None, want_lse: bool = False, lse=None,
+                        ws=None, stream=None):
+    """Unmasked attention of q [Nq, H, D] over k, v [Nk, H, D] (bf16).
+    Returns (out bf16 [Nq, H, D], lse float32 [H, Nq] or None)."""
+    _bits(q, "q"), _bits(k, "k"), _bits(v, "v")
+    Nq, H, D = q.shape
+    Nk = k.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((H, Nq), dtype=torch.float32, device=dev)
+    if ws is None:
+        nb = wkv_attention_workspace_bytes(Nq, Nk, H, D)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    st = _attn(_ptr(q), _ptr(k), _ptr(v), Nq, Nk, H, D, float(scale), _ptr(out), _ptr(lse),
+               _ptr(ws), ws.numel(), _stream(stream))
+    _check("wkv_chunk_attention", st)
+    return out, lse

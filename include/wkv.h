@@ -1,0 +1,220 @@
+/*
+ * wkv.h -- C ABI of libwkv, the KV-memory hot path of WorldKV-style
+ * autoregressive video world models, hand-written HIP for gfx950 (MI355X).
+ *
+ * Sources, cited by page title and section:
+ *   [WorldKV]   "WorldKV: Efficient World Memory with World Retrieval and
+ *               Compression": Sec. 4.2 World Retrieval, Sec. 4.3 World
+ *               Compression, Sec. 5.1 Implementation Details.
+ *   [WorldPager] WorldPager summary: abstract and Fig. 2 (int4 KV store,
+ *               retrieval from the extrapolated camera pose).
+ *   [WorldAttention] WorldAttention breakdown: scaled dot-product attention of
+ *               the current chunk over visible keys; the index-mapping and
+ *               contiguous-copy stages of its kernel section.
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns. K / V / Q tensors are
+ *     token-major and contiguous: [rows][H][D], one row = H*D*2 bytes.
+ *   - Pointers are DEVICE memory unless marked [host]. Every device pointer
+ *     must be 16-byte aligned. The caller allocates and owns every buffer; the
+ *     library never allocates and never frees device memory.
+ *   - Every call enqueues its kernels on the given stream (a hipStream_t; NULL
+ *     = the default stream) and returns without synchronising. WKV_OK means
+ *     "enqueued". A device-side fault surfaces at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *   - All argument checks run on the host before anything is enqueued. A
+ *     non-OK status enqueues nothing and leaves every output untouched; the
+ *     reason is available from wkv_last_error() (thread-local text).
+ *   - Calls are stateless and reentrant; ordering is the stream's.
+ *   - Supported shapes: D in {64, 128}; H >= 1; H*D <= 8192.
+ */
+#ifndef WKV_H_
+#define WKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV_ABI_VERSION 1
+
+typedef void* wkv_stream_t; /* hipStream_t */
+
+typedef enum {
+  WKV_OK = 0,
+  WKV_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  WKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
+  WKV_ERR_RATIO = 3,       /* keep ratio outside [0, 1] or NaN               */
+  WKV_ERR_K = 4,           /* top-k count < 1 or pose history not 1 or 2     */
+  WKV_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned        */
+  WKV_ERR_WORKSPACE = 6,   /* workspace too small                            */
+  WKV_ERR_UNSUPPORTED = 7, /* head dim / dtype not supported                 */
+  WKV_ERR_HIP = 8          /* the HIP runtime rejected a launch              */
+} wkv_status;
+
+/* Camera pose of a chunk: translation and yaw (radians). [WorldKV] Sec. 4.2
+ * indexes each stored chunk by the camera state at its generation time. */
+typedef struct {
+  float x, y, z, yaw;
+} wkv_pose;
+
+/* A run of window rows: k, v bf16 [n][H][D] (device). n may be 0 (then k, v
+ * may be NULL). */
+typedef struct {
+  const uint16_t* k;
+  const uint16_t* v;
+  int32_t n;
+} wkv_segment;
+
+enum { WKV_BANK_BF16 = 0, WKV_BANK_INT4_G32 = 1 };
+
+/* The store of compressed chunks ([WorldKV] Sec. 4.2: evicted chunks are kept
+ * in memory, each indexed by its camera state). M chunks of Lc rows each.
+ *   WKV_BANK_BF16:     k, v = bf16 [M][Lc][H][D]; k_scale, v_scale unused.
+ *   WKV_BANK_INT4_G32: k, v = uint8 [M][Lc][H][D/2], element d of a (row,
+ *                      head) in byte d/2, low nibble for even d, read as a
+ *                      signed 4-bit integer q in [-8, 7]; k_scale, v_scale =
+ *                      bf16 [M][Lc][H][D/32], one scale per 32 consecutive
+ *                      elements along D. Value = bf16_RNE(float(q) * scale).
+ *                      ([WorldPager] abstract / Fig. 2: the KV memory is
+ *                      stored as int4.) */
+typedef struct {
+  int32_t dtype;
+  int32_t M;
+  int32_t Lc;
+  const void* k;
+  const void* v;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+} wkv_bank;
+
+/* ABI version of the loaded library (WKV_ABI_VERSION). */
+int32_t wkv_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread. */
+const char* wkv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * World Compression ([WorldKV] Sec. 4.3 "World Compression Mechanism").
+ *
+ * A unit is one evicted chunk at one layer: F frames x T tokens, frame 0 is
+ * the anchor. For every non-anchor token (frame f >= 1, position j) the score
+ *     s[(f-1)*T + j] = (1/H) * sum_h cos(K[f,j,h,:], K[0,j,h,:])
+ * is the head-mean cosine to the anchor key at the same position (0 when a
+ * norm is 0), computed in float64. The n_keep = wkv_keep_count(F, T, r)
+ * lowest (score, pooled index) pairs are retained (ties go to the lower
+ * index, NaN orders last). The compressed unit is the T anchor rows followed
+ * by the retained rows in ascending source order, for K and V alike.
+ * ------------------------------------------------------------------------ */
+
+/* [host] n_keep = round-half-away(r * (F-1) * T) in float64, clamped to
+ * [0, (F-1)*T]. Returns -1 for invalid arguments. Rows per compressed unit
+ * are T + n_keep. */
+int32_t wkv_keep_count(int32_t F, int32_t T, float r);
+
+/* [host] Workspace bytes wkv_compress_chunk needs for B units. */
+size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T);
+
+/* Compress B contiguous units.
+ *   k, v       bf16 [B][F*T][H][D]            inputs
+ *   k_out,
+ *   v_out      bf16 [B][Lc][H][D]             outputs, Lc = T + n_keep
+ *   kept_idx   int32 [B][Lc]                  output: in-unit source row of
+ *                                             every output row, ascending
+ *   scores     double [B][(F-1)*T] or NULL    optional output
+ *   ws         >= wkv_compress_workspace_bytes(B, F, T) bytes (may be NULL
+ *              when that is 0)
+ * Limits: 1 <= B; 2 <= F <= 8; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1. */
+wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
+                              int32_t F, int32_t T, int32_t H, int32_t D,
+                              float r, uint16_t* k_out, uint16_t* v_out,
+                              int32_t* kept_idx, double* scores, void* ws,
+                              size_t ws_bytes, wkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * World Retrieval by camera pose ([WorldKV] Sec. 4.2 retrieval equation
+ * R = Top-k(sim(a_cur, a_i)); Sec. 5.1: distance = squared L2 translation +
+ * geodesic rotation, each normalised over the candidate set, smallest first).
+ *
+ * For every stored chunk i, in float64:
+ *   dt_i = (x_i-x_q)^2 + (y_i-y_q)^2 + (z_i-z_q)^2
+ *   dr_i = |wrap(yaw_i - yaw_q)|, wrap into (-pi, pi]
+ *   D_i  = minmax(dt)_i + minmax(dr)_i    (a term is 0 when its range is 0)
+ * The k_eff = min(k, M) smallest (D_i, i) pairs are returned, sorted by
+ * ascending chunk index.
+ *
+ * The query pose: n_hist = 1 -> query_hist[0]; n_hist = 2 -> extrapolated
+ * linearly from query_hist[0] (previous) and query_hist[1] (last):
+ * q = last + (last - prev), yaw = wrap(yaw_l + wrap(yaw_l - yaw_p)), formed
+ * in float64 and stored as float ([WorldPager] Fig. 2: the retrieval set of
+ * the next chunk comes from the extrapolated pose).
+ *   bank_poses  wkv_pose [M]          device, 1 <= M <= 8192
+ *   query_hist  wkv_pose [n_hist]     [host]
+ *   out_idx     int32 [k_eff]         output, ascending chunk ids
+ *   out_dist    double [k_eff]        optional output (NULL ok): D_i
+ *   out_query   wkv_pose [1]          optional output (NULL ok): query used
+ * ------------------------------------------------------------------------ */
+wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
+                         const wkv_pose* query_hist, int32_t n_hist, int32_t k,
+                         int32_t* out_idx, double* out_dist,
+                         wkv_pose* out_query, wkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Window assembly ([WorldKV] Sec. 4.2: retrieved KV is inserted back into the
+ * native attention window without re-encoding; Sec. 5.1: the window is
+ * sink | retrieval | recent | denoising; [WorldAttention] kernel section:
+ * selected KV is copied into one contiguous buffer before attention).
+ *
+ * Writes win_k / win_v bf16 [Nk][H][D] with
+ *   rows [0, n_s)                          = sink
+ *   rows [n_s + i*Lc, n_s + (i+1)*Lc)      = bank chunk retrieved_idx[i],
+ *                                            i = 0..n_ret-1 (int4 banks are
+ *                                            dequantised on the fly)
+ *   then recent[0], ..., recent[n_recent-1], then current,
+ * Nk = n_s + n_ret*Lc + sum(recent[].n) + current.n, which must not exceed
+ * win_rows. A retrieved id outside [0, M) yields zero rows (no fault).
+ *   sink, current  [host] wkv_segment
+ *   bank           [host] wkv_bank (device arrays inside)
+ *   retrieved_idx  int32 [n_ret] device (e.g. out_idx of wkv_pose_topk)
+ *   recent         [host] wkv_segment [n_recent], 0 <= n_recent <= 14
+ * ------------------------------------------------------------------------ */
+wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,
+                               const int32_t* retrieved_idx, int32_t n_ret,
+                               const wkv_segment* recent, int32_t n_recent,
+                               const wkv_segment* current, int32_t H, int32_t D,
+                               uint16_t* win_k, uint16_t* win_v,
+                               int64_t win_rows, wkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Chunk attention ([WorldAttention]: scaled dot-product attention of the
+ * current chunk's Nq queries over Nk visible keys, 1/sqrt(d) scaling,
+ * repeated at every denoising step; [WorldKV] Sec. 1 / 5.2: the denoising
+ * chunk attends to the assembled window).
+ *   O[i,h,:] = sum_j softmax_j(scale * <Q[i,h,:], K[j,h,:]>) V[j,h,:]
+ * No mask; query and key head counts are equal. bf16 MFMA products with
+ * float32 accumulation and softmax; O is rounded to bf16 (RNE).
+ *   q    bf16 [Nq][H][D];  k, v  bf16 [Nk][H][D];  out  bf16 [Nq][H][D]
+ *   lse  float [H][Nq] optional (NULL ok): natural-log log-sum-exp of the
+ *        scaled scores of every query row
+ *   scale <= 0 selects 1/sqrt(D)
+ *   ws   workspace for split-key partials; wkv_attention_workspace_bytes()
+ *        gives the size for the library's preferred split. With less (or
+ *        NULL) the call uses as many splits as fit, down to none.
+ * Limits: 1 <= Nq, 1 <= Nk, Nk < 2^31 / H.
+ * ------------------------------------------------------------------------ */
+size_t wkv_attention_workspace_bytes(int32_t Nq, int32_t Nk, int32_t H,
+                                     int32_t D);
+
+wkv_status wkv_chunk_attention(const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, int32_t Nq, int32_t Nk,
+                               int32_t H, int32_t D, float scale,
+                               uint16_t* out, float* lse, void* ws,
+                               size_t ws_bytes, wkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV_H_ */

@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(all calls here fail validation, so no GPU is touched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv.h")
+LIB = os.path.join(ROOT, "ar_video_world_amd", "libwkv.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libwkv.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(wkv_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def w():
+    import ar_video_world_amd.wkv as w
+    return w
+
+
+def test_every_declared_symbol_is_exported(w):
+    lib = C.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(w.EXPORTS)
+
+
+def test_abi_version_and_keep_count(w):
+    assert w.wkv_abi_version() == 1
+    assert w.wkv_keep_count(3, 880, 0.5) == 880
+    assert w.wkv_keep_count(3, 880, 0.25) == 440
+    assert w.wkv_keep_count(3, 1560, 0.25) == 780
+    assert w.wkv_keep_count(2, 3, 0.5) == 2
+    assert w.wkv_keep_count(2, 5, 0.1) == 1
+    assert w.wkv_keep_count(3, 7, 1.0) == 14
+    assert w.wkv_keep_count(3, 7, float("nan")) == -1
+    assert w.wkv_keep_count(3, 7, 1.5) == -1
+    assert w.wkv_keep_count(1, 7, 0.5) == -1
+    assert w.wkv_compress_workspace_bytes(4, 3, 880) == 4 * 1760 * 8
+    assert w.wkv_attention_workspace_bytes(0, 1, 1, 128) == 0
+
+
+def test_keep_count_matches_oracle(w):
+    from oracle import wkv_oracle as O
+    for F in (2, 3, 4):
+        for T in (1, 7, 64, 880, 1560):
+            for r in (0.0, 0.1, 0.25, 0.3333, 0.5, 0.75, 0.9, 1.0):
+                assert w.wkv_keep_count(F, T, r) == O.keep_count(F, T, r)
+
+
+A = 0x10000          # a 16-byte aligned stand-in pointer (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+def st(fn, *args):
+    return fn(*args)
+
+
+def test_compress_validation(w):
+    f = w._compress
+    ok = [A, A, 1, 3, 64, 2, 64, 0.5, A, A, A, None, A, 1 << 20, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["k", "v", "B", "F", "T", "H", "D", "r", "ko", "vo", "ki", "sc", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(k=None) == 1
+    assert call(ki=None) == 1
+    assert call(D=96) == 7
+    assert call(H=0) == 2
+    assert call(H=129, D=64) == 2
+    assert call(F=1) == 2
+    assert call(F=5) == 2
+    assert call(T=0) == 2
+    assert call(T=8193, F=2) == 2
+    assert call(r=1.5) == 3
+    assert call(r=-0.1) == 3
+    assert call(r=float("nan")) == 3
+    assert call(k=MIS) == 5
+    assert call(sc=MIS) == 5
+    assert call(ws=None, wsb=0) == 6
+    assert call(wsb=100) == 6
+    assert "workspace" in w.wkv_last_error()
+
+
+def test_pose_validation(w):
+    f = w._pose_topk
+    q = (w.wkv_pose * 2)(w.wkv_pose(0, 0, 0, 0), w.wkv_pose(1, 1, 1, 0.1))
+    assert f(None, 4, q, 1, 2, A, None, None, None) == 1
+    assert f(A, 4, None, 1, 2, A, None, None, None) == 1
+    assert f(A, 4, q, 1, 2, None, None, None, None) == 1
+    assert f(A, 0, q, 1, 2, A, None, None, None) == 2
+    assert f(A, 8193, q, 1, 2, A, None, None, None) == 2
+    assert f(A, 4, q, 1, 0, A, None, None, None) == 4
+    assert f(A, 4, q, 3, 2, A, None, None, None) == 4
+    assert f(A, 4, q, 1, 2, MIS, None, None, None) == 5
+    assert f(A, 4, q, 1, 2, A, MIS, None, None) == 5
+
+
+def test_assemble_validation(w):
+    f = w._assemble
+    seg = w.wkv_segment(A, A, 10)
+    bad = w.wkv_segment(None, A, 10)
+    mis = w.wkv_segment(MIS, A, 10)
+    neg = w.wkv_segment(A, A, -1)
+    bank = w.wkv_bank(0, 4, 8, A, A, None, None)
+    bank_i4 = w.wkv_bank(1, 4, 8, A, A, None, None)
+    bank_bad = w.wkv_bank(7, 4, 8, A, A, None, None)
+    rec = (w.wkv_segment * 2)(seg, seg)
+    R = C.byref
+    assert f(None, R(bank), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 1
+    assert f(R(seg), R(bank), A, 2, rec, 2, R(seg), 2, 64, None, A, 100, None) == 1
+    assert f(R(seg), R(bank), A, 2, rec, 2, R(seg), 2, 96, A, A, 100, None) == 7
+    assert f(R(seg), R(bank), A, -1, rec, 2, R(seg), 2, 64, A, A, 100, None) == 2
+    assert f(R(seg), R(bank), A, 2, rec, 15, R(seg), 2, 64, A, A, 100, None) == 2
+    assert f(R(seg), None, A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 1
+    assert f(R(seg), R(bank), None, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 1
+    assert f(R(bad), R(bank), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 1
+    assert f(R(neg), R(bank), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 2
+    assert f(R(mis), R(bank), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 5
+    assert f(R(seg), R(bank_bad), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 7
+    assert f(R(seg), R(bank_i4), A, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 1
+    assert f(R(seg), R(bank), MIS, 2, rec, 2, R(seg), 2, 64, A, A, 100, None) == 5
+    # window needs 10 + 2*8 + 20 + 10 = 56 rows
+    assert f(R(seg), R(bank), A, 2, rec, 2, R(seg), 2, 64, A, A, 55, None) == 2
+    assert "56" in w.wkv_last_error()
+
+
+def test_attention_validation(w):
+    f = w._attn
+    assert f(None, A, A, 4, 4, 2, 64, 0.0, A, None, None, 0, None) == 1
+    assert f(A, A, A, 4, 4, 2, 64, 0.0, None, None, None, 0, None) == 1
+    assert f(A, A, A, 0, 4, 2, 64, 0.0, A, None, None, 0, None) == 2
+    assert f(A, A, A, 4, 0, 2, 64, 0.0, A, None, None, 0, None) == 2
+    assert f(A, A, A, 4, 4, 2, 80, 0.0, A, None, None, 0, None) == 7
+    assert f(A, A, A, 4, 1 << 24, 1024, 64, 0.0, A, None, None, 0, None) == 2
+    assert f(A, MIS, A, 4, 4, 2, 64, 0.0, A, None, None, 0, None) == 5
+    assert f(A, A, A, 4, 4, 2, 64, 0.0, A, MIS, None, 0, None) == 5
+    assert f(A, A, A, 4, 4, 2, 64, float("inf"), A, None, None, 0, None) == 2

@@ -1,0 +1,120 @@
+"""GPU parity of wkv_chunk_attention against the fp64 oracle (WorldAttention
+scaled dot-product attention; WorldKV Sec. 1 / 5.2): max-abs <= 2e-2 and
+mean-abs <= 2e-3 on unit-scale inputs, at small sizes on every query and at
+the full 1.3B / 14B sizes on sampled query rows (the ragged last tile is
+always sampled). Exact cases: one key returns its value row."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import wkv_synth as S
+from oracle import wkv_oracle as O
+from tests.parity import check_attention, gpu_ready, np_bits, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ready(), reason="needs the built library and a GPU")]
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def w():
+    import ar_video_world_amd.wkv as w
+    return w
+
+
+def qkv(cfg, Nq, Nk, H, D, device=DEV):
+    q = S.queries(cfg, 0, Nq, H, D, device=device)
+    k, v = S.segment_kv(cfg, 7, Nk, H, D, device=device)
+    return q, k, v
+
+
+def attn_case(w, Nq, Nk, H, D, label, sample=None, small_ws=False, cfg=21):
+    q, k, v = qkv(cfg, Nq, Nk, H, D)
+    say("attention", label, "Nq", Nq, "Nk", Nk, "H", H, "D", D, "small_ws", small_ws)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV) if small_ws else None
+    o, lse = w.wkv_chunk_attention(q, k, v, want_lse=True, ws=ws)
+    torch.cuda.synchronize()
+    rows = np.arange(Nq) if sample is None else np.asarray(sample)
+    qb = np_bits(q)[rows]
+    ro, rl = O.chunk_attention(qb, np_bits(k), np_bits(v))
+    stats = check_attention(o[torch.as_tensor(rows, device=DEV)], ro)
+    lerr = float(np.max(np.abs(lse.cpu().numpy()[:, rows] - rl)))
+    assert lerr < 1e-3, lerr
+    stats["lse_max_abs"] = lerr
+    print(f"  {label}: {stats}", flush=True)
+    return o, lse, stats
+
+
+def test_tiny_config(w):
+    # 1 sink chunk + 2 retrieved compressed + 1 recent + current: 832 keys
+    attn_case(w, 192, 832, 2, 64, "tiny")
+
+
+@pytest.mark.parametrize("Nq,Nk,H,D", [(200, 1000, 3, 128), (1, 1, 1, 128), (129, 65, 2, 64),
+                                       (64, 4097, 1, 128), (300, 63, 5, 128), (17, 2000, 2, 64)])
+def test_ragged(w, Nq, Nk, H, D):
+    attn_case(w, Nq, Nk, H, D, f"ragged {Nq}x{Nk}x{H}x{D}")
+
+
+def test_split_matches_unsplit(w):
+    # few query tiles and many keys: the library splits the key range
+    Nq, Nk, H, D = 128, 20000, 2, 128
+    assert w.wkv_attention_workspace_bytes(Nq, Nk, H, D) > 0
+    o1, l1, _ = attn_case(w, Nq, Nk, H, D, "split", sample=range(0, 128, 3))
+    o2, l2, _ = attn_case(w, Nq, Nk, H, D, "unsplit", sample=range(0, 128, 3), small_ws=True)
+    d = (o1.float() - o2.float()).abs().max().item()
+    assert d < 1e-2, d
+
+
+def test_single_key_returns_value_exactly(w):
+    q, k, v = qkv(22, 70, 1, 3, 128)
+    say("attention", "single key")
+    o, _ = w.wkv_chunk_attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), v.expand(70, 3, 128).contiguous().view(torch.int16))
+
+
+def test_equal_keys_give_mean_value(w):
+    Nk, H, D = 300, 2, 128
+    q = S.queries(23, 0, 40, H, D, device=DEV)
+    k = S.segment_kv(23, 1, 1, H, D, device=DEV)[0].expand(Nk, H, D).contiguous()
+    v = S.segment_kv(23, 2, Nk, H, D, device=DEV)[1]
+    say("attention", "equal keys")
+    o, _ = w.wkv_chunk_attention(q, k, v)
+    torch.cuda.synchronize()
+    mean = O.bf16_to_f64(np_bits(v)).mean(axis=0)
+    err = np.abs(o.float().cpu().numpy() - mean[None]).max()
+    assert err < 2e-3, err
+
+
+def test_explicit_scale(w):
+    q, k, v = qkv(24, 100, 500, 2, 128)
+    say("attention", "explicit scale")
+    o, _ = w.wkv_chunk_attention(q, k, v, scale=0.3)
+    torch.cuda.synchronize()
+    ro, _ = O.chunk_attention(np_bits(q), np_bits(k), np_bits(v), scale=0.3)
+    check_attention(o, ro)
+
+
+def test_13b_full_size_sampled(w):
+    Nq, Nk, H, D = 2640, 15840, 12, 128
+    sample = list(range(0, 64)) + list(range(1290, 1300)) + list(range(2560, 2640))
+    attn_case(w, Nq, Nk, H, D, "1.3B r=0.5", sample=sample)
+
+
+def test_14b_full_size_sampled(w):
+    Nq, Nk, H, D = 4680, 32760, 40, 128
+    sample = list(range(0, 24)) + list(range(4600, 4680))
+    attn_case(w, Nq, Nk, H, D, "14B r=0.25", sample=sample)
+
+
+def test_deterministic(w):
+    q, k, v = qkv(25, 2640, 15840, 12, 128)
+    say("attention", "determinism")
+    a, _ = w.wkv_chunk_attention(q, k, v)
+    b, _ = w.wkv_chunk_attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
