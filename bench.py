@@ -1,0 +1,342 @@
+"""Benchmark of the WorldKV KV-memory hot path on one GPU.
+
+One step is one pass of the whole path for one denoising chunk at one layer:
+  1. World Compression of the chunk leaving the recent window (1 unit),
+  2. pose top-k retrieval over the stored chunks,
+  3. window assembly sink | retrieved | recent | current,
+  4. chunk attention of the current queries over the window, once per
+     denoising step of the chunk.
+Inputs are seeded synthetic tensors resident in HBM before the timed region;
+several input sets rotate so the bandwidth-bound calls are not served from the
+last-level cache. After the timed region the CPU oracle runs on a bounded
+sample of the same workload (reported as ``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1.3b]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("chunk-attention TFLOP/s + compress/gather GB/s; "
+          "per-chunk denoise-step latency")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+# Workloads: heads x head dim, tokens per frame, frames per chunk, keep ratio,
+# stored chunks, retrieved k, recent chunks, denoising steps, int4 bank.
+CONFIGS = {
+    "tiny": dict(H=2, D=64, T=64, F=3, r=0.5, M=8, k=2, n_recent=1, S=1, int4=False,
+                 name="tiny: 2 heads x d64, 3x64-token chunks, 8 stored chunks, "
+                      "window sink + 2 retrieved (r=0.5) + 1 recent + current"),
+    "1.3b": dict(H=12, D=128, T=880, F=3, r=0.5, M=20, k=3, n_recent=2, S=1, int4=False,
+                 name="1.3B-class single layer: 12 heads x d128, 3x880-token chunks, "
+                      "20 stored chunks, window sink + 3 retrieved (r=0.5) + 2 recent "
+                      "+ current"),
+    "14b": dict(H=40, D=128, T=1560, F=3, r=0.25, M=120, k=6, n_recent=2, S=4, int4=False,
+                name="14B-class single layer: 40 heads x d128, 3x1560-token chunks, "
+                     "120 stored chunks, window sink + 6 retrieved (r=0.25) + 2 recent "
+                     "+ current, 4 denoising steps"),
+    "int4": dict(H=12, D=128, T=880, F=3, r=0.5, M=1000, k=4, n_recent=2, S=1, int4=True,
+                 name="long-rollout int4 store: 12 heads x d128, 3x880-token chunks, "
+                      "1000 stored int4 chunks (r=0.5, g32 bf16 scales), extrapolated "
+                      "query pose, window sink + 4 retrieved + 2 recent + current"),
+}
+CFG_SEED = {"tiny": 1, "1.3b": 2, "14b": 4, "int4": 5}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="1.3b", choices=sorted(CONFIGS))
+    ap.add_argument("--r", type=float, default=None, help="override the keep ratio")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="query rows in the oracle's attention sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(c, Lc, n_keep, Nk):
+    """Bytes the method must move (per call): compress and assemble."""
+    R = c["H"] * c["D"] * 2
+    N = (c["F"] - 1) * c["T"]
+    s_read = c["F"] * c["T"] if 0 < n_keep < N else Lc
+    comp = R * (s_read + Lc + 2 * Lc)
+    ret_rows = c["k"] * Lc
+    other_rows = Nk - ret_rows
+    if c["int4"]:
+        hd = c["H"] * c["D"]
+        per_bank_row = 2 * (hd * 0.5 + (hd // 32) * 2) + 2 * R
+        asm = 4 * R * other_rows + per_bank_row * ret_rows
+    else:
+        asm = 4 * R * Nk
+    return comp, asm
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {a.gpus} is not "
+              "supported (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ar_video_world_amd.wkv as w
+    import wkv_synth as S
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    c = dict(CONFIGS[a.config])
+    if a.r is not None:
+        c["r"] = a.r
+    seed = CFG_SEED[a.config]
+    H, D, T, F, r = c["H"], c["D"], c["T"], c["F"], c["r"]
+    FT = F * T
+    n_keep = w.wkv_keep_count(F, T, r)
+    Lc = T + n_keep
+    M, k, nrec, nsteps = c["M"], c["k"], c["n_recent"], c["S"]
+    Nq = FT
+    Nk = FT + k * Lc + nrec * FT + FT
+    stream = torch.cuda.Stream()
+
+    with torch.cuda.stream(stream):
+        # ---- stored bank (compressed chunks) and its poses
+        if c["int4"]:
+            kp, vp, ks, vs = S.int4_bank(seed, M, Lc, H, D, device=dev)
+            bank = {"k": kp, "v": vp, "k_scale": ks, "v_scale": vs}
+        else:
+            bk = torch.empty((M, Lc, H, D), dtype=torch.bfloat16, device=dev)
+            bv = torch.empty_like(bk)
+            for m in range(M):
+                bk[m], bv[m] = S.segment_kv(seed, 100 + m, Lc, H, D, device=dev)
+            bank = {"k": bk, "v": bv}
+        walk = S.pose_walk(seed, M + 3)
+        poses = walk[1:M + 1].contiguous().to(dev)
+        if c["int4"]:
+            qhist = [walk[M + 1].tolist(), walk[M + 2].tolist()]  # extrapolated
+        else:
+            qhist = [walk[M + 2].tolist()]
+
+        # ---- rotating per-step input sets
+        sets = []
+        for i in range(a.sets):
+            ek, ev = S.chunk_kv(seed, 1000 + i, 0, F, T, H, D, device=dev)
+            segs = [S.segment_kv(seed, 2000 + 10 * i + j, FT, H, D, device=dev)
+                    for j in range(nrec + 2)]
+            qs = [S.queries(seed, s, Nq, H, D, device=dev, layer=i) for s in range(nsteps)]
+            sets.append(dict(
+                ek=ek, ev=ev, sink=segs[0], recent=segs[1:1 + nrec], cur=segs[-1], q=qs,
+                ko=torch.empty((Lc, H, D), dtype=torch.bfloat16, device=dev),
+                vo=torch.empty((Lc, H, D), dtype=torch.bfloat16, device=dev),
+                kidx=torch.empty((Lc,), dtype=torch.int32, device=dev),
+                wk=torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev),
+                wv=torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)))
+        cws = torch.empty(max(w.wkv_compress_workspace_bytes(1, F, T), 16),
+                          dtype=torch.uint8, device=dev)
+        aws = torch.empty(max(w.wkv_attention_workspace_bytes(Nq, Nk, H, D), 16),
+                          dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+        def step(i, ev=None):
+            s = sets[i % len(sets)]
+            if ev is not None:
+                ev[0].record()
+            w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                 kept_idx=s["kidx"], ws=cws)
+            if ev is not None:
+                ev[1].record()
+            idx, _, _ = w.wkv_pose_topk(poses, qhist, k, want_dist=False)
+            if ev is not None:
+                ev[2].record()
+            w.wkv_assemble_window(s["sink"], bank, idx, s["recent"], s["cur"], H, D,
+                                  win_k=s["wk"], win_v=s["wv"])
+            if ev is not None:
+                ev[3].record()
+            for j in range(nsteps):
+                if ev is not None:
+                    ev[4 + 2 * j].record()
+                w.wkv_chunk_attention(s["q"][j], s["wk"], s["wv"], out=s["out"], ws=aws)
+                if ev is not None:
+                    ev[5 + 2 * j].record()
+
+        for i in range(a.warmup):
+            step(i)
+        torch.cuda.synchronize()
+
+        # ---- timed region: wall clock over exactly K steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall = t1 - t0
+
+        # ---- per-call durations, from HIP events on the launch stream
+        nev = 4 + 2 * nsteps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+               for _ in range(a.steps)]
+        for i in range(a.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        t_comp = [e[0].elapsed_time(e[1]) for e in evs]
+        t_pose = [e[1].elapsed_time(e[2]) for e in evs]
+        t_asm = [e[2].elapsed_time(e[3]) for e in evs]
+        t_att = [e[4 + 2 * j].elapsed_time(e[5 + 2 * j]) for e in evs for j in range(nsteps)]
+
+        if a.copy_probe:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+
+    ms_per_step = wall / a.steps * 1e3
+    comp_b, asm_b = algorithmic_bytes(c, Lc, n_keep, Nk)
+    flops = 4.0 * Nq * Nk * D * H
+    mean = statistics.fmean
+    att_ms = mean(t_att)
+    att_tflops = flops / (att_ms * 1e-3) / 1e12
+    comp_ms, asm_ms, pose_ms = mean(t_comp), mean(t_asm), mean(t_pose)
+    splits = w.wkv_attention_workspace_bytes(Nq, Nk, H, D) > 0
+
+    rec = {
+        "metric": METRIC,
+        "value": round(a.steps / wall, 3),
+        "unit": "chunk-steps/s (one step = compress + pose top-k + assemble + "
+                f"{nsteps} attention pass{'es' if nsteps > 1 else ''})",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded rho-mixture keys, N(0,1) values and queries, "
+                "random-walk poses)",
+        "config": {"workload": c["name"], "heads": H, "head_dim": D, "tokens_per_frame": T,
+                   "frames_per_chunk": F, "keep_ratio": r, "compressed_rows": Lc,
+                   "stored_chunks": M, "retrieved": k, "window_keys": Nk, "queries": Nq,
+                   "denoise_steps": nsteps, "int4_bank": c["int4"], "parallelism": "none",
+                   "input_sets": a.sets},
+        "breakdown": {
+            "compress_us": round(comp_ms * 1e3, 2),
+            "compress_GBps": round(comp_b / (comp_ms * 1e-3) / 1e9, 1),
+            "compress_bytes": comp_b,
+            "pose_topk_us": round(pose_ms * 1e3, 2),
+            "assemble_us": round(asm_ms * 1e3, 2),
+            "assemble_GBps": round(asm_b / (asm_ms * 1e-3) / 1e9, 1),
+            "assemble_bytes": int(asm_b),
+            "attention_us": round(att_ms * 1e3, 2),
+            "attention_TFLOPs": round(att_tflops, 1),
+            "attention_flop": flops,
+            "attention_split_keys": splits,
+            "event_step_ms": round(comp_ms + pose_ms + asm_ms + att_ms * nsteps, 4),
+        },
+        "roofline": {
+            "kernel": "wkv_chunk_attention" + (" (fwd + split merge)" if splits else ""),
+            "bound": "mfma",
+            "achieved": round(att_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(a, c, sets[0], bank, poses, qhist, Nq, Nk, Lc)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(a, c, s, bank, poses, qhist, Nq, Nk, Lc):
+    """The oracle, as it stands, on a bounded sample of one step's work."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import wkv_oracle as O
+
+    def bits(t):
+        import torch
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    F, T, r, k, nsteps = c["F"], c["T"], c["r"], c["k"], c["S"]
+    ek, ev = bits(s["ek"]), bits(s["ev"])
+    P = poses.cpu().numpy()
+    t0 = time.perf_counter()
+    O.compress_chunk(ek, ev, F, T, r)
+    t1 = time.perf_counter()
+    if len(qhist) == 2:
+        q = O.pose_extrapolate(np.asarray(qhist[0], np.float32), np.asarray(qhist[1], np.float32))
+    else:
+        q = np.asarray(qhist[0], np.float32)
+    idx, _ = O.pose_topk(P, q, k)
+    t2 = time.perf_counter()
+    # only the retrieved chunks leave the device; the oracle indexes them 0..k-1
+    sel = [int(i) for i in idx]
+    ridx = np.arange(len(sel))
+    if c["int4"]:
+        kp, vp = bank["k"][sel].cpu().numpy(), bank["v"][sel].cpu().numpy()
+        kss, vss = bits(bank["k_scale"][sel]), bits(bank["v_scale"][sel])
+        t_deq = time.perf_counter()
+        hb = O.dequant_bank_chunks(kp, vp, kss, vss, ridx)
+        t_deq = time.perf_counter() - t_deq
+    else:
+        hb = (bits(bank["k"][sel]), bits(bank["v"][sel]))
+        t_deq = 0.0
+    sink = (bits(s["sink"][0]), bits(s["sink"][1]))
+    rec = [(bits(x), bits(y)) for x, y in s["recent"]]
+    cur = (bits(s["cur"][0]), bits(s["cur"][1]))
+    t3 = time.perf_counter()
+    wk, wv = O.assemble_window(sink, hb, ridx, rec, cur)
+    t4 = time.perf_counter()
+    rows = min(Nq, a.cpu_rows)
+    qb = bits(s["q"][0])[:rows]
+    t5 = time.perf_counter()
+    O.chunk_attention(qb, wk, wv)
+    t6 = time.perf_counter()
+    t_att_full = (t6 - t5) * Nq / rows
+    t_step = (t1 - t0) + (t2 - t1) + t_deq + (t4 - t3) + nsteps * t_att_full
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p["num_threads"] for p in blas] or [1])
+    return {
+        "value": round(1.0 / t_step, 6),
+        "unit": "chunk-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle: compress of 1 unit, pose top-k over {len(P)} poses "
+                   f"and window assembly ({Nk} rows) in full; attention on {rows} of {Nq} "
+                   f"query rows x {c['H']} heads over the full window, scaled by "
+                   f"{Nq}/{rows} and by {nsteps} denoising step(s); BLAS threads = cores, "
+                   "elementwise work single-threaded"),
+        "seconds": {"compress": round(t1 - t0, 3), "pose_topk": round(t2 - t1, 4),
+                    "assemble": round(t4 - t3 + t_deq, 3), "attention_sample": round(t6 - t5, 3),
+                    "step_estimate": round(t_step, 3)},
+    }
+
+
+if __name__ == "__main__":
+    main()
