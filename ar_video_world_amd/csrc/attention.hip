@@ -19,8 +19,11 @@
 //     when staged, so each lane reads its 8 keys as one 16-byte LDS load.
 //   * K rows in LDS use an XOR swizzle of 16-byte chunks so the permuted row
 //     reads are free of bank conflicts.
-//   * Softmax in base 2: p = exp2(s * scale*log2e - m). The O rescale is
-//     skipped (exactly) for a wave whose running max did not change.
+//   * Softmax in base 2: p = exp2(s * scale*log2e - m). The running max m is
+//     only raised (and O, l rescaled) when a tile's max exceeds it by more
+//     than 2^8; in between p may reach 2^8, which changes nothing exactly.
+//   * K/V tiles are fetched with raw buffer loads: one scalar descriptor per
+//     tile and fixed per-thread offsets, rows past the window read as zero.
 //   * Long key ranges with few query tiles are split over blocks; each split
 //     writes unnormalised fp32 partials plus (m, l) and a merge kernel
 //     combines them with the log-sum-exp identity.
@@ -43,8 +46,20 @@ constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;  // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer descriptor (stride 0): loads at byte offsets >= nrec return 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
 
 // MFMA row rho of a 32-key tile holds key perm(rho) of that tile.
 __device__ __forceinline__ int key_perm(int rho) {
@@ -66,12 +81,50 @@ __device__ __forceinline__ int xcd_remap(int L, int G) {
 }
 
 template <int D>
-struct Smem {
-  static constexpr int VP = kBN + 8;        // V^T row pitch (bf16)
-  static constexpr int K_ELEMS = kBN * D;   // swizzled, no pad
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
+struct Tile {
+  static constexpr int KCH = D / 8;                       // 16-byte chunks per row
+  static constexpr int ROW = D * 2;                       // bytes per row of one head
+  static constexpr int BYTES = kBN * ROW;                 // one K or V tile
+  static constexpr int STAGE = 2 * BYTES;                 // K tile, then V tile
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW;        // rows per wave-wide 1 KiB load
+  static constexpr int LOADS = BYTES / 1024 / (kThreads / 64);  // per wave and operand
 };
+
+// V rows: chunk c of key r is stored at position c ^ vswz(r). The transpose
+// reads of the P*V operand touch 4 consecutive keys x one 64-byte quarter of
+// the row per half-wave; the rotation puts those 4 quarters on disjoint banks.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * (r & 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16 bytes per lane from global (raw buffer, zero past nrec) straight into
+// LDS at lds + 16 * lane.
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group the
+// lanes' 4-element chunks are concatenated and lane j receives elements j,
+// j+16, j+32, j+48 of that sequence.
+__device__ __forceinline__ uint2 lds_read_tr(const uint8_t* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// max over the lane pair (l, l ^ 32) with one VALU lane swap.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
@@ -79,12 +132,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ V, int Nq, int Nk, int H, float c,
     uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ opart,
     float2* __restrict__ mlpart, int nsplit, int kps) {
-  using S = Smem<D>;
-  constexpr int KS = D / 16;             // k-steps of the QK product
-  constexpr int DT = D / 32;             // d tiles of the PV product
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int KLD = kBN * KCH / kThreads;  // K chunks staged per thread
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
+  using T = Tile<D>;
+  constexpr int KS = D / 16;   // k-steps of the QK product
+  constexpr int DT = D / 32;   // d tiles of the PV product
+  constexpr int KCH = T::KCH;
+  // Two stages in two separate arrays: every LDS read and every direct load
+  // below names its stage at compile time, so the compiler can see that the
+  // loads in flight never alias the stage being read and does not wait on
+  // them before the reads.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[T::STAGE];
 
   const int ntq = (Nq + kBM - 1) / kBM;
   const int W = xcd_remap(blockIdx.x, gridDim.x);
@@ -113,97 +170,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // Staging assignments.
-  // K: chunk cidx = r*256 + tid -> key cidx / KCH, chunk cidx % KCH.
-  // V: 4 keys (4*kg .. +3) x 8 dims (8*dch .. +7) per thread.
-  const int kg = tid & 15, dch = tid >> 4;
-  const bool vact = dch < D / 8;
-  uint4 kreg[KLD];
-  uint4 vreg[4];
+  // Direct-to-LDS staging: each wave-wide load fills 1 KiB of the tile, lane
+  // l writing the 16 bytes at row (l / KCH), position (l % KCH) of its rows.
+  // The lane fetches the global chunk that the row's swizzle puts there.
+  // Offsets are relative to the tile's first row of this head.
+  uint32_t kvo[T::LOADS], vvo[T::LOADS];
+#pragma unroll
+  for (int r = 0; r < T::LOADS; ++r) {
+    const int row = (wave * T::LOADS + r) * T::ROWS_PER_LOAD + lane / KCH;
+    const int pos = lane % KCH;
+    kvo[r] = (uint32_t)((row * (int)HD + (pos ^ kswz<D>(row)) * 8) * 2);
+    vvo[r] = (uint32_t)((row * (int)HD + (pos ^ vswz<D>(row)) * 8) * 2);
+  }
+  auto issue_tile = [&](int kb, uint8_t* stage) {
+    const size_t base = (size_t)kb * HD + (size_t)h * D;
+    const uint32_t nrec = (uint32_t)(((size_t)(Nk - kb) * HD - (size_t)h * D) * 2);
+    const rsrc_t rk = make_rsrc(K + base, nrec);
+    const rsrc_t rv = make_rsrc(V + base, nrec);
+    uint8_t* dk = stage + wave * T::LOADS * 1024;
+    uint8_t* dv = dk + T::BYTES;
+#pragma unroll
+    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rk, dk + r * 1024, kvo[r]);
+#pragma unroll
+    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rv, dv + r * 1024, vvo[r]);
+  };
 
-  auto load_tile = [&](int kb) {
+  // LDS read offsets. S^T operand: row kt*32 + prow (prow = key_perm(l32)),
+  // chunk (2ks + g) swizzled; the swizzle depends on the row's low 4 bits
+  // only, so it is the same for both 32-key halves.
+  const int prow = key_perm(l32);
+  uint32_t koff[KS];
 #pragma unroll
-    for (int r = 0; r < KLD; ++r) {
-      const int cidx = r * kThreads + tid;
-      const int key = cidx / KCH, ch = cidx % KCH;
-      const int gk = kb + key;
-      kreg[r] = (gk < kend)
-                    ? *reinterpret_cast<const uint4*>(K + (size_t)gk * HD + (size_t)h * D + ch * 8)
-                    : make_uint4(0, 0, 0, 0);
-    }
+  for (int ks = 0; ks < KS; ++ks)
+    koff[ks] = (uint32_t)(prow * T::ROW + (((2 * ks + g) ^ kswz<D>(prow)) * 16));
+  // P*V operand (transpose reads): lane i of 16-lane group G reads keys
+  // kb0 + i/4 (kb0 = kt*32 + 16mm + 8g + 4h, a multiple of 4) at columns
+  // dt*32 + 16*(G%2) + 4*(i%4) .. +3, so lane j gets 4 keys of column
+  // dt*32 + 16*(G%2) + j = dt*32 + l32.
+  const int trow = (lane & 15) >> 2;
+  const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  uint32_t voff[DT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gk = kb + 4 * kg + i;
-      vreg[i] = (vact && gk < kend)
-                    ? *reinterpret_cast<const uint4*>(V + (size_t)gk * HD + (size_t)h * D + dch * 8)
-                    : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * S::BUF;
-    uint16_t* VT = Ks + S::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < KLD; ++r) {
-      const int cidx = r * kThreads + tid;
-      const int key = cidx / KCH, ch = cidx % KCH;
-      *reinterpret_cast<uint4*>(Ks + key * D + ((ch ^ kswz<D>(key)) * 8)) = kreg[r];
-    }
-    if (vact) {
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
-        uint2 lo, hi;
-        lo.x = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-        lo.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-        hi.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-        hi.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-        const int d = dch * 8 + 2 * w;
-        *reinterpret_cast<uint2*>(VT + d * S::VP + 4 * kg) = lo;
-        *reinterpret_cast<uint2*>(VT + (d + 1) * S::VP + 4 * kg) = hi;
-      }
-    }
-  };
+  for (int dt = 0; dt < DT; ++dt)
+    voff[dt] = (uint32_t)((8 * g + trow) * T::ROW + (((4 * dt + tchunk) ^ vswz<D>(trow)) * 16) +
+                          (lane & 1) * 8);
 
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m = -INFINITY;  // running max of s*c (base-2 domain)
+  float m = -INFINITY;  // running reference max of s*c (base-2 domain)
   float lsum = 0.f;     // this lane's share of the denominator
 
-  // Row of the 32-key MFMA tile this lane feeds (A operand of S^T).
-  const int prow = key_perm(l32);
-
   const int nblk = (kend - kbeg + kBN - 1) / kBN;
-  load_tile(kbeg);
-  store_tile(0);
+  if (nblk > 0) issue_tile(kbeg, stage0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  for (int it = 0; it < nblk; ++it) {
+  // One key tile: prefetch the next tile into the other stage, then S^T,
+  // softmax and O^T on the tile in `rd`.
+  auto tile = [&](int it, const uint8_t* rd, uint8_t* wr) {
     const int kb = kbeg + it * kBN;
-    const int cur = it & 1;
-    const bool has_next = it + 1 < nblk;
-    if (has_next) load_tile(kb + kBN);
+    if (it + 1 < nblk) issue_tile(kb + kBN, wr);
 
-    const uint16_t* Ks = smem + cur * S::BUF;
-    const uint16_t* VT = Ks + S::K_ELEMS;
+    const uint8_t* Ks = rd;
+    const uint8_t* Vs = rd + T::BYTES;
 
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
-      const int r = kt * 32 + prow;
-      const uint16_t* krow = Ks + r * D;
-      const int sw = kswz<D>(r);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow + (((2 * ks + g) ^ sw) * 8));
+        const uint4 a = *reinterpret_cast<const uint4*>(Ks + kt * 32 * T::ROW + koff[ks]);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], s[kt], 0, 0, 0);
       }
     }
@@ -224,13 +265,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
+    mx = max_halves(mx);
+    // Lazy rescale: the reference max only moves (and O, l are rescaled)
+    // when some row's tile max exceeds it by more than kSlack in the base-2
+    // domain; otherwise p <= 2^kSlack, which fp32 and bf16 carry as well.
+    // O and l always share one reference, so the result is unchanged.
+    const float m_cand = fmaxf(m, mx * c);
+    if (__any(m_cand > m + kSlack)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_cand);
+      m = m_cand;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    }
 
     bf16x8 pb[2][2];
-    float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -238,19 +289,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         f32x8 pv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * mm + e], c, -m_new));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * mm + e], c, -m));
           pv[e] = p;
-          ps += p;
+          lsum += p;
         }
         pb[kt][mm] = __builtin_convertvector(pv, bf16x8);
       }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-    }
 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -258,16 +302,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              VT + (dt * 32 + l32) * S::VP + kt * 32 + 16 * mm + 8 * g);
+          const uint8_t* vb = Vs + (kt * 32 + 16 * mm) * T::ROW + voff[dt];
+          const uint2 lo = lds_read_tr(vb);
+          const uint2 hi = lds_read_tr(vb + 4 * T::ROW);
+          const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[kt][mm], o[dt], 0, 0, 0);
         }
 
-    if (has_next) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
     __syncthreads();
+  };
+  for (int it = 0; it < nblk; it += 2) {
+    tile(it, stage0, stage1);
+    if (it + 1 < nblk) tile(it + 1, stage1, stage0);
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float ltot = sum_halves(lsum);
   if (q >= Nq) return;
   if (nsplit == 1) {
     const float inv = 1.0f / ltot;
@@ -357,15 +407,17 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int N
 
 }  // namespace
 
-// Split the key range only when the (q-tile, head) grid cannot give every CU
-// two blocks; each split keeps >= 8 key tiles.
+// Two 4-wave blocks fit on a CU. The key range is split (in powers of two,
+// each split keeping >= 8 key tiles) only until the grid covers about 90% of
+// those resident slots: fewer splits mean less partial traffic to merge.
 AttnPlan attention_plan(int Nq, int Nk, int H, int D, int num_cus) {
   (void)D;
   AttnPlan p;
   const long long tiles = (long long)((Nq + kBM - 1) / kBM) * H;
+  const long long slots = 2LL * num_cus;
   const int kblocks = (Nk + kBN - 1) / kBN;
   int splits = 1;
-  while (tiles * splits < 2LL * num_cus && kblocks / (splits * 2) >= 8) splits *= 2;
+  while (tiles * splits * 10 < slots * 9 && kblocks / (splits * 2) >= 8) splits *= 2;
   const int kb_per = (kblocks + splits - 1) / splits;
   p.keys_per_split = kb_per * kBN;
   p.splits = (kblocks + kb_per - 1) / kb_per;
