@@ -4,26 +4,34 @@
 // online softmax: running max m, denominator l, unnormalised output o).
 //
 // gfx950 design. One block = 4 waves = 128 queries of one head; each wave owns
-// 32 queries and walks the key range in tiles of 64 keys staged in LDS
-// (double-buffered, next tile's global loads in flight during the current
-// tile's math).
+// 32 queries and walks the key range in tiles of 64 keys.
+//   * K/V tiles go from global memory straight into LDS with raw buffer loads
+//     (buffer_load ... lds): no register staging, no VALU, rows past the
+//     window read as zero. K is staged one tile ahead of V in two K and two V
+//     stages, each its own LDS array, so the compiler can see that loads in
+//     flight never alias the stages being read.
 //   * S^T = K_tile * Q^T on v_mfma_f32_32x32x16_bf16: the 32x32 accumulator
 //     layout puts one query per lane column, so the softmax row statistics of
-//     a query live in two lanes (lane, lane^32) and need one cross-lane op.
+//     a query live in two lanes (lane, lane^32), combined by v_permlane32_swap.
 //   * The rows of each 32-key MFMA tile are fed in a fixed permutation of the
 //     keys chosen so that accumulator elements 8m..8m+7 of a lane are exactly
 //     the 8 consecutive keys that lane must supply as the B operand of the
 //     P*V MFMA: P^T goes from accumulator to operand by a bf16 conversion, with
 //     no shuffle. The same permutation indexes V^T, so the sum is unchanged.
-//   * O^T += V^T * P^T on the same MFMA; V is transposed into LDS ([d][key])
-//     when staged, so each lane reads its 8 keys as one 16-byte LDS load.
-//   * K rows in LDS use an XOR swizzle of 16-byte chunks so the permuted row
-//     reads are free of bank conflicts.
-//   * Softmax in base 2: p = exp2(s * scale*log2e - m). The running max m is
-//     only raised (and O, l rescaled) when a tile's max exceeds it by more
-//     than 2^8; in between p may reach 2^8, which changes nothing exactly.
-//   * K/V tiles are fetched with raw buffer loads: one scalar descriptor per
-//     tile and fixed per-thread offsets, rows past the window read as zero.
+//   * O^T += V^T * P^T on the same MFMA; the V^T operand comes from row-major V
+//     in LDS through transposing reads (ds_read_b64_tr_b16).
+//   * K and V rows in LDS use XOR swizzles of 16-byte chunks so that the row
+//     reads and the transposing reads are free of bank conflicts.
+//   * VALU work per score is the floor of what softmax needs: Q is
+//     pre-multiplied by scale*log2(e) (bf16), and each S^T accumulator chain
+//     starts from -mref (a register block holding the reference max), so the
+//     MFMA emits the base-2 exponent directly; then exp2, bf16 conversion and
+//     a bf16 dot2 row sum of exactly the weights the P*V product uses.
+//   * The reference max only moves when a tile's max exceeds it by more than
+//     2^8 (and on the first tile); in between p may reach 2^8, which changes
+//     nothing exactly. O and l always share the reference.
+//   * The S^T product of tile t+1 is issued between the softmax of tile t and
+//     its P*V product, so one wave has MFMA work independent of its VALU work.
 //   * Long key ranges with few query tiles are split over blocks; each split
 //     writes unnormalised fp32 partials plus (m, l) and a merge kernel
 //     combines them with the log-sum-exp identity.
@@ -136,12 +144,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int DT = D / 32;   // d tiles of the PV product
   constexpr int KCH = T::KCH;
-  // Two stages in two separate arrays: every LDS read and every direct load
-  // below names its stage at compile time, so the compiler can see that the
-  // loads in flight never alias the stage being read and does not wait on
-  // them before the reads.
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[T::STAGE];
+  // K is staged one tile ahead of V (the S^T product of tile t+1 overlaps
+  // the softmax of tile t), in two K and two V stages. Each stage is its own
+  // array and every access names its array at compile time, so the compiler
+  // can see that loads in flight never alias the stages being read.
+  __shared__ __attribute__((aligned(1024))) uint8_t kst0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kst1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst1[T::BYTES];
 
   const int ntq = (Nq + kBM - 1) / kBM;
   const int W = xcd_remap(blockIdx.x, gridDim.x);
@@ -166,7 +176,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 16);
       if (q >= Nq) u = make_uint4(0, 0, 0, 0);
-      qf[ks] = as_bf16x8(u);
+      // Q * scale * log2(e), rounded to bf16: S^T then comes out of the MFMA
+      // in the base-2 domain.
+      const bf16x8 x = as_bf16x8(u);
+      f32x8 xf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[e] = (float)x[e] * c;
+      qf[ks] = __builtin_convertvector(xf, bf16x8);
     }
   }
 
@@ -182,17 +198,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kvo[r] = (uint32_t)((row * (int)HD + (pos ^ kswz<D>(row)) * 8) * 2);
     vvo[r] = (uint32_t)((row * (int)HD + (pos ^ vswz<D>(row)) * 8) * 2);
   }
-  auto issue_tile = [&](int kb, uint8_t* stage) {
+  auto issue = [&](const uint16_t* src, int kb, uint8_t* stage, const uint32_t (&vo)[T::LOADS]) {
     const size_t base = (size_t)kb * HD + (size_t)h * D;
     const uint32_t nrec = (uint32_t)(((size_t)(Nk - kb) * HD - (size_t)h * D) * 2);
-    const rsrc_t rk = make_rsrc(K + base, nrec);
-    const rsrc_t rv = make_rsrc(V + base, nrec);
-    uint8_t* dk = stage + wave * T::LOADS * 1024;
-    uint8_t* dv = dk + T::BYTES;
+    const rsrc_t rs = make_rsrc(src + base, nrec);
+    uint8_t* dst = stage + wave * T::LOADS * 1024;
 #pragma unroll
-    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rk, dk + r * 1024, kvo[r]);
-#pragma unroll
-    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rv, dv + r * 1024, vvo[r]);
+    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rs, dst + r * 1024, vo[r]);
   };
 
   // LDS read offsets. S^T operand: row kt*32 + prow (prow = key_perm(l32)),
@@ -220,34 +232,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m = -INFINITY;  // running reference max of s*c (base-2 domain)
-  float lsum = 0.f;     // this lane's share of the denominator
+  float mref = 0.f;    // reference max of s*scale*log2(e) for this lane's query
+  bool first = true;   // the first tile sets mref
+  float lsum = 0.f;    // this lane's share of the denominator
 
   const int nblk = (kend - kbeg + kBN - 1) / kBN;
-  if (nblk > 0) issue_tile(kbeg, stage0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
 
-  // One key tile: prefetch the next tile into the other stage, then S^T,
-  // softmax and O^T on the tile in `rd`.
-  auto tile = [&](int it, const uint8_t* rd, uint8_t* wr) {
-    const int kb = kbeg + it * kBN;
-    if (it + 1 < nblk) issue_tile(kb + kBN, wr);
-
-    const uint8_t* Ks = rd;
-    const uint8_t* Vs = rd + T::BYTES;
-
-    f32x16 s[2];
+  // S^T of one tile from the K stage `ks_` (Q^T in registers).
+  // The accumulator of every S^T chain starts from `seed` = -mref (the
+  // lane's query reference max, repeated), so the MFMA emits
+  // s*scale*log2(e) - mref directly.
+  f32x16 seed;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) seed[e] = 0.f;
+  auto qk = [&](const uint8_t* ks_, f32x16 (&st)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(ks_ + kt * 32 * T::ROW + koff[0]);
+      st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[0], seed, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks + kt * 32 * T::ROW + koff[ks]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], s[kt], 0, 0, 0);
+      for (int ks = 1; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks_ + kt * 32 * T::ROW + koff[ks]);
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], st[kt], 0, 0, 0);
       }
     }
+  };
+
+  // Prologue: K(0), V(0), K(1) in flight, then S^T(0).
+  f32x16 sc[2];
+  if (nblk > 0) {
+    issue(K, kbeg, kst0, kvo);
+    issue(V, kbeg, vst0, vvo);
+  }
+  if (nblk > 1) issue(K, kbeg + kBN, kst1, kvo);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  qk(kst0, sc);
+  __syncthreads();  // kst0 is refilled by the first iteration
+
+  // Iteration t: loads K(t+2) and V(t+1); softmax of S(t) (registers)
+  // overlapped with S^T(t+1) from K stage kc; O^T += V(t) P(t) from V stage vc.
+  auto tile = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kd, uint8_t* vd) {
+    const int kb = kbeg + it * kBN;
+    if (it + 2 < nblk) issue(K, kb + 2 * kBN, kd, kvo);
+    if (it + 1 < nblk) issue(V, kb + kBN, vd, vvo);
 
     // Mask keys past the end of this block's range (last tile only).
     if (kb + kBN > kend) {
@@ -256,7 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + kt * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-          if (key >= kend) s[kt][e] = -INFINITY;
+          if (key >= kend) sc[kt][e] = -INFINITY;
         }
     }
 
@@ -264,57 +292,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kt][e]);
     mx = max_halves(mx);
-    // Lazy rescale: the reference max only moves (and O, l are rescaled)
-    // when some row's tile max exceeds it by more than kSlack in the base-2
-    // domain; otherwise p <= 2^kSlack, which fp32 and bf16 carry as well.
-    // O and l always share one reference, so the result is unchanged.
-    const float m_cand = fmaxf(m, mx * c);
-    if (__any(m_cand > m + kSlack)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_cand);
-      m = m_cand;
+    // Lazy rescale. S' = s*scale*log2(e) - mref. The reference mref only
+    // moves (up, to the row's max) when some row of the wave has S' > kSlack,
+    // and on the first tile, where it is set to the tile's row max; then O
+    // and l are rescaled and S' is re-based. Otherwise p = 2^S' <= 2^kSlack,
+    // which fp32 and bf16 carry as well. O and l always share mref, so the
+    // result is unchanged.
+    if (__any(first || mx > kSlack)) {
+      const float delta = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      mref += delta;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kt][e] -= delta;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) seed[e] = -mref;
     }
+    first = false;
 
-    bf16x8 pb[2][2];
+    // S^T of the next tile (its K stage landed last iteration). On the last
+    // tile this reads a stale stage and the result is dropped.
+    f32x16 sn[2];
+    qk(kc, sn);
+
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         f32x8 pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * mm + e], c, -m));
-          pv[e] = p;
-          lsum += p;
-        }
-        pb[kt][mm] = __builtin_convertvector(pv, bf16x8);
-      }
-
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
+        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sc[kt][8 * mm + e]);
+        const bf16x8 b = __builtin_convertvector(pv, bf16x8);
+        // row sum of the bf16 weights that the P*V product uses
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), ones, lsum, false);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint8_t* vb = Vs + (kt * 32 + 16 * mm) * T::ROW + voff[dt];
+          const uint8_t* vb = vc + (kt * 32 + 16 * mm) * T::ROW + voff[dt];
           const uint2 lo = lds_read_tr(vb);
           const uint2 hi = lds_read_tr(vb + 4 * T::ROW);
           const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[kt][mm], o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), b, o[dt], 0, 0, 0);
         }
+      }
+    sc[0] = sn[0];
+    sc[1] = sn[1];
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(t+2), V(t+1) have landed
     __syncthreads();
   };
   for (int it = 0; it < nblk; it += 2) {
-    tile(it, stage0, stage1);
-    if (it + 1 < nblk) tile(it + 1, stage1, stage0);
+    tile(it, kst1, vst0, kst0, vst1);
+    if (it + 1 < nblk) tile(it + 1, kst0, vst1, kst1, vst0);
   }
 
   const float ltot = sum_halves(lsum);
@@ -331,7 +372,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         w.y = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(op + dt * 32 + 8 * i + 4 * g) = w;
       }
-    if (lse && g == 0) lse[(size_t)h * Nq + q] = (m + log2f(ltot)) * kLn2;
+    if (lse && g == 0) lse[(size_t)h * Nq + q] = (mref + log2f(ltot)) * kLn2;
   } else {
     const size_t row = ((size_t)split * H + h) * Nq + q;
     float* pp = opart + row * D;
@@ -343,7 +384,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                o[dt][4 * i + 3]);
         *reinterpret_cast<float4*>(pp + dt * 32 + 8 * i + 4 * g) = w;
       }
-    if (g == 0) mlpart[row] = make_float2(m, ltot);
+    if (g == 0) mlpart[row] = make_float2(mref, ltot);
   }
 }
 

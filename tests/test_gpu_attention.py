@@ -31,6 +31,17 @@ def qkv(cfg, Nq, Nk, H, D, device=DEV):
     return q, k, v
 
 
+def lse_tolerance(D):
+    """Bound on the log-sum-exp error. The kernel rounds Q*scale*log2(e) to
+    bf16 (relative error uniform in +-2^-9 per element), so a score of
+    unit-scale Q, K moves by a random amount of std
+    2^-9/sqrt(3) * scale * sqrt(D) in natural-log units, which is 2^-9/sqrt(3)
+    for scale = 1/sqrt(D); the LSE is a weighted mean of such moves. Allow
+    6 sigma."""
+    sigma = 2.0 ** -9 / math.sqrt(3.0) * (1.0 / math.sqrt(D)) * math.sqrt(D)
+    return 6.0 * sigma
+
+
 def attn_case(w, Nq, Nk, H, D, label, sample=None, small_ws=False, cfg=21):
     q, k, v = qkv(cfg, Nq, Nk, H, D)
     say("attention", label, "Nq", Nq, "Nk", Nk, "H", H, "D", D, "small_ws", small_ws)
@@ -42,7 +53,7 @@ def attn_case(w, Nq, Nk, H, D, label, sample=None, small_ws=False, cfg=21):
     ro, rl = O.chunk_attention(qb, np_bits(k), np_bits(v))
     stats = check_attention(o[torch.as_tensor(rows, device=DEV)], ro)
     lerr = float(np.max(np.abs(lse.cpu().numpy()[:, rows] - rl)))
-    assert lerr < 1e-3, lerr
+    assert lerr < lse_tolerance(D), (lerr, lse_tolerance(D))
     stats["lse_max_abs"] = lerr
     print(f"  {label}: {stats}", flush=True)
     return o, lse, stats
