@@ -22,16 +22,15 @@
 //     in LDS through transposing reads (ds_read_b64_tr_b16).
 //   * K and V rows in LDS use XOR swizzles of 16-byte chunks so that the row
 //     reads and the transposing reads are free of bank conflicts.
-//   * VALU work per score is the floor of what softmax needs: Q is
-//     pre-multiplied by scale*log2(e) (bf16), and each S^T accumulator chain
-//     starts from -mref (a register block holding the reference max), so the
-//     MFMA emits the base-2 exponent directly; then exp2, bf16 conversion and
-//     a bf16 dot2 row sum of exactly the weights the P*V product uses.
-//   * The reference max only moves when a tile's max exceeds it by more than
-//     2^8 (and on the first tile); in between p may reach 2^8, which changes
-//     nothing exactly. O and l always share the reference.
-//   * The S^T product of tile t+1 is issued between the softmax of tile t and
-//     its P*V product, so one wave has MFMA work independent of its VALU work.
+//   * Softmax in base 2 with a fixed per-row reference: p = exp2(s*c - mref),
+//     c = scale*log2(e), converted to bf16, and the row sum is a bf16 dot2 of
+//     exactly the weights the P*V product uses. There is no per-tile row max:
+//     a range guard on the tile's row sums (rare branch) moves mref to the
+//     row max only when some weight would approach the fp32/bf16 range or a
+//     row has not accumulated any weight yet. O and l always share mref, so
+//     the result does not depend on where it sits.
+//   * The S^T product of tile t+1 is issued ahead of the softmax of tile t,
+//     so one wave has MFMA work independent of its VALU work.
 //   * Long key ranges with few query tiles are split over blocks; each split
 //     writes unnormalised fp32 partials plus (m, l) and a merge kernel
 //     combines them with the log-sum-exp identity.
@@ -54,7 +53,8 @@ constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr float kBigSum = 1073741824.0f;     // 2^30: largest accepted tile row sum
+constexpr float kTinySum = 8.673617e-19f;    // 2^-60: smallest accepted running row sum
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -176,13 +176,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 16);
       if (q >= Nq) u = make_uint4(0, 0, 0, 0);
-      // Q * scale * log2(e), rounded to bf16: S^T then comes out of the MFMA
-      // in the base-2 domain.
-      const bf16x8 x = as_bf16x8(u);
-      f32x8 xf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xf[e] = (float)x[e] * c;
-      qf[ks] = __builtin_convertvector(xf, bf16x8);
+      qf[ks] = as_bf16x8(u);
     }
   }
 
@@ -232,26 +226,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float mref = 0.f;    // reference max of s*scale*log2(e) for this lane's query
-  bool first = true;   // the first tile sets mref
+  float mref = 0.f;    // reference for s*scale*log2(e) of this lane's query
   float lsum = 0.f;    // this lane's share of the denominator
 
   const int nblk = (kend - kbeg + kBN - 1) / kBN;
 
   // S^T of one tile from the K stage `ks_` (Q^T in registers).
-  // The accumulator of every S^T chain starts from `seed` = -mref (the
-  // lane's query reference max, repeated), so the MFMA emits
-  // s*scale*log2(e) - mref directly.
-  f32x16 seed;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) seed[e] = 0.f;
   auto qk = [&](const uint8_t* ks_, f32x16 (&st)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(ks_ + kt * 32 * T::ROW + koff[0]);
-      st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[0], seed, 0, 0, 0);
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) {
+      for (int e = 0; e < 16; ++e) st[kt][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(ks_ + kt * 32 * T::ROW + koff[ks]);
         st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], st[kt], 0, 0, 0);
       }
@@ -288,65 +275,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kt][e]);
-    mx = max_halves(mx);
-    // Lazy rescale. S' = s*scale*log2(e) - mref. The reference mref only
-    // moves (up, to the row's max) when some row of the wave has S' > kSlack,
-    // and on the first tile, where it is set to the tile's row max; then O
-    // and l are rescaled and S' is re-based. Otherwise p = 2^S' <= 2^kSlack,
-    // which fp32 and bf16 carry as well. O and l always share mref, so the
-    // result is unchanged.
-    if (__any(first || mx > kSlack)) {
-      const float delta = first ? mx : fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      mref += delta;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[kt][e] -= delta;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) seed[e] = -mref;
-    }
-    first = false;
-
     // S^T of the next tile (its K stage landed last iteration). On the last
     // tile this reads a stale stage and the result is dropped.
     f32x16 sn[2];
     qk(kc, sn);
 
+    // p = 2^(s*c - mref) as bf16, and the tile's row sum of exactly those
+    // weights (this lane's half of the row).
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8 pb[2][2];
+    float ts = 0.f;
+    auto weights = [&]() {
+      ts = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          f32x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * mm + e], c, -mref));
+          const bf16x8 b = __builtin_convertvector(pv, bf16x8);
+          pb[kt][mm] = b;
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), ones, ts, false);
+        }
+    };
+    weights();
+    // Range guard. The reference mref stays where it is while every half-row
+    // tile sum is <= 2^30 (no weight near the fp32/bf16 range) and every row
+    // has accumulated >= 2^-60 (what dominates it has not underflowed).
+    // Otherwise the row's reference moves to its max (up only, once weight
+    // has accumulated; O and l are rescaled by the same factor, or reset if
+    // nothing has accumulated) and the weights are recomputed. O and l always
+    // share mref, so the result is the same for any reference. Both halves
+    // of a row decide on row-wide quantities, so they always agree.
+    if (__any(!(ts <= kBigSum) || !(sum_halves(lsum + ts) >= kTinySum))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kt][e]);
+      mx = max_halves(mx) * c;
+      const bool acc = sum_halves(lsum) > 0.f;
+      float mnew = acc ? fmaxf(mref, mx) : mx;
+      if (!(mnew > -INFINITY)) mnew = mref;  // every key of the row masked
+      const float alpha = acc ? __builtin_amdgcn_exp2f(mref - mnew) : 0.f;
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      weights();
+    }
+    lsum += ts;
+
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sc[kt][8 * mm + e]);
-        const bf16x8 b = __builtin_convertvector(pv, bf16x8);
-        // row sum of the bf16 weights that the P*V product uses
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), ones, lsum, false);
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const uint8_t* vb = vc + (kt * 32 + 16 * mm) * T::ROW + voff[dt];
           const uint2 lo = lds_read_tr(vb);
           const uint2 hi = lds_read_tr(vb + 4 * T::ROW);
           const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), b, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[kt][mm], o[dt], 0, 0, 0);
         }
-      }
     sc[0] = sn[0];
     sc[1] = sn[1];
 

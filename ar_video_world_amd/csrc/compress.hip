@@ -12,9 +12,10 @@
 //            per-head cosine in LDS; the block then averages over heads in a
 //            fixed order. The anchor slice already sits in registers, so the
 //            score kernel also writes the anchor rows of k_out.
-//   select - one 1024-thread block per unit: radix select of the n_keep-th
-//            smallest (score, index) key, stable compaction by block scan,
-//            writes kept_idx.
+//   select - one block per unit, sized to the pooled count (256, 512 or 1024
+//            threads, 8 keys each): radix select of the n_keep-th smallest
+//            (score, index) key, stable compaction by block scan, writes
+//            kept_idx.
 //   gather - one wave per output row: copies the kept K rows (non-anchor) and
 //            all kept V rows with 16-byte loads and stores.
 #include "wkv_common.hpp"
@@ -134,10 +135,10 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
   }
 }
 
-constexpr int kSelBlock = 1024;
-constexpr int kSelKPT = 8;  // N <= 8192
+constexpr int kSelKPT = 8;  // N <= 8 * block size
 
 // grid: B. Writes kept_idx[b][0..Lc).
+template <int kSelBlock>
 __global__ __launch_bounds__(kSelBlock) void compress_select_kernel(
     const double* __restrict__ scores, int N, int T, int n_keep,
     int32_t* __restrict__ kept_idx, int Lc) {
@@ -267,8 +268,15 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                    : dispatch_score_F<64>(k, B, F, T, H, TT, scores, k_out, Lc, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(compress_select_kernel, dim3(B), dim3(kSelBlock), 0, s,
-                     scores, N, T, n_keep, kept_idx, Lc);
+  if (N <= 256 * kSelKPT)
+    hipLaunchKernelGGL((compress_select_kernel<256>), dim3(B), dim3(256), 0, s, scores, N, T,
+                       n_keep, kept_idx, Lc);
+  else if (N <= 512 * kSelKPT)
+    hipLaunchKernelGGL((compress_select_kernel<512>), dim3(B), dim3(512), 0, s, scores, N, T,
+                       n_keep, kept_idx, Lc);
+  else
+    hipLaunchKernelGGL((compress_select_kernel<1024>), dim3(B), dim3(1024), 0, s, scores, N, T,
+                       n_keep, kept_idx, Lc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows_per_block = (kGatherBlock / 64) * kRowsPerWave;

@@ -1,11 +1,12 @@
 // World Retrieval by camera pose (WorldKV Sec. 4.2 retrieval equation,
 // Sec. 5.1 distance recipe; WorldPager Fig. 2 for the extrapolated query).
 //
-// One 1024-thread block: every thread forms the query pose, computes the
-// float64 translation and rotation distances of up to 8 stored chunks, the
-// block reduces their min and max, forms the normalised sum, and the shared
-// radix select keeps the k smallest (distance, index) pairs, written in
-// ascending chunk order. Floating-point contraction is off in this file so
+// One block sized to the bank (one wave up to 64 chunks, 256 threads up to
+// 1024, 1024 threads up to 8192): every thread forms the query pose,
+// computes the float64 translation and rotation distances of its stored
+// chunks, the block reduces their min and max, forms the normalised sum, and
+// the shared radix select keeps the k smallest (distance, index) pairs,
+// written in ascending chunk order. Floating-point contraction is off in this file so
 // every distance is the same sequence of correctly rounded IEEE operations
 // the definition states.
 #pragma clang fp contract(off)
@@ -18,8 +19,6 @@ namespace wkv {
 
 namespace {
 
-constexpr int kBlock = 1024;
-constexpr int kKPT = 8;  // M <= 8192
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kPi = 3.1415926535897932384626433832795;
 
@@ -37,6 +36,7 @@ struct PoseArgs {
   int n_hist;
 };
 
+template <int BLOCK>
 __device__ __forceinline__ double block_reduce(double v, bool is_max, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -48,16 +48,17 @@ __device__ __forceinline__ double block_reduce(double v, bool is_max, double* re
   if (lane == 0) red[wave] = v;
   __syncthreads();
   double r = red[0];
-  for (int w = 1; w < kBlock / 64; ++w) r = is_max ? fmax(r, red[w]) : fmin(r, red[w]);
+  for (int w = 1; w < BLOCK / 64; ++w) r = is_max ? fmax(r, red[w]) : fmin(r, red[w]);
   return r;
 }
 
-__global__ __launch_bounds__(kBlock) void pose_topk_kernel(
+template <int BLOCK, int KPT>
+__global__ __launch_bounds__(BLOCK) void pose_topk_kernel(
     const float4* __restrict__ poses, int M, PoseArgs qa, int k_eff,
     int32_t* __restrict__ out_idx, double* __restrict__ out_dist,
     float4* __restrict__ out_query) {
   __shared__ SelectShared sh;
-  __shared__ double red[kBlock / 64];
+  __shared__ double red[BLOCK / 64];
   const int tid = threadIdx.x;
 
   double qx = qa.qx, qy = qa.qy, qz = qa.qz, qyaw = qa.qyaw;
@@ -72,12 +73,12 @@ __global__ __launch_bounds__(kBlock) void pose_topk_kernel(
   const float fqx = (float)qx, fqy = (float)qy, fqz = (float)qz, fqyaw = (float)qyaw;
   if (tid == 0 && out_query) *out_query = make_float4(fqx, fqy, fqz, fqyaw);
 
-  double dtr[kKPT], drot[kKPT];
-  bool valid[kKPT];
+  double dtr[KPT], drot[KPT];
+  bool valid[KPT];
   double tmin = INFINITY, tmax = -INFINITY, rmin = INFINITY, rmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kKPT; ++i) {
-    const int p = tid * kKPT + i;
+  for (int i = 0; i < KPT; ++i) {
+    const int p = tid * KPT + i;
     valid[i] = p < M;
     dtr[i] = 0.0;
     drot[i] = 0.0;
@@ -94,42 +95,42 @@ __global__ __launch_bounds__(kBlock) void pose_topk_kernel(
       rmax = fmax(rmax, drot[i]);
     }
   }
-  tmin = block_reduce(tmin, false, red);
-  tmax = block_reduce(tmax, true, red);
-  rmin = block_reduce(rmin, false, red);
-  rmax = block_reduce(rmax, true, red);
+  tmin = block_reduce<BLOCK>(tmin, false, red);
+  tmax = block_reduce<BLOCK>(tmax, true, red);
+  rmin = block_reduce<BLOCK>(rmin, false, red);
+  rmax = block_reduce<BLOCK>(rmax, true, red);
   const double trng = tmax - tmin, rrng = rmax - rmin;
 
-  uint64_t key[kKPT];
-  double dist[kKPT];
+  uint64_t key[KPT];
+  double dist[KPT];
 #pragma unroll
-  for (int i = 0; i < kKPT; ++i) {
+  for (int i = 0; i < KPT; ++i) {
     const double a = (tmax == tmin) ? 0.0 : (dtr[i] - tmin) / trng;
     const double r = (rmax == rmin) ? 0.0 : (drot[i] - rmin) / rrng;
     dist[i] = a + r;
     key[i] = valid[i] ? order_key(dist[i]) : ~0ull;
   }
-  bool keep[kKPT];
+  bool keep[KPT];
   int kc;
   if (k_eff >= M) {
     kc = 0;
 #pragma unroll
-    for (int i = 0; i < kKPT; ++i) {
+    for (int i = 0; i < KPT; ++i) {
       keep[i] = valid[i];
       kc += keep[i] ? 1 : 0;
     }
   } else {
     uint64_t prefix, mask;
     int rank;
-    block_radix_select<kBlock, kKPT>(key, valid, k_eff, sh, &prefix, &mask, &rank);
-    kc = block_keep_flags<kBlock, kKPT>(key, valid, prefix, mask, rank, sh, keep);
+    block_radix_select<BLOCK, KPT>(key, valid, k_eff, sh, &prefix, &mask, &rank);
+    kc = block_keep_flags<BLOCK, KPT>(key, valid, prefix, mask, rank, sh, keep);
   }
   int tot;
-  int pos = block_exclusive_scan<kBlock>(kc, sh, &tot);
+  int pos = block_exclusive_scan<BLOCK>(kc, sh, &tot);
 #pragma unroll
-  for (int i = 0; i < kKPT; ++i) {
+  for (int i = 0; i < KPT; ++i) {
     if (keep[i] && pos < k_eff) {  // never past the k_eff outputs
-      out_idx[pos] = tid * kKPT + i;
+      out_idx[pos] = tid * KPT + i;
       if (out_dist) out_dist[pos] = dist[i];
     }
     pos += keep[i] ? 1 : 0;
@@ -147,9 +148,17 @@ hipError_t pose_topk_launch(const void* poses, int M, const float* last,
   qa.px = prev ? prev[0] : 0.f; qa.py = prev ? prev[1] : 0.f;
   qa.pz = prev ? prev[2] : 0.f; qa.pyaw = prev ? prev[3] : 0.f;
   qa.n_hist = n_hist;
-  hipLaunchKernelGGL(pose_topk_kernel, dim3(1), dim3(kBlock), 0, s,
-                     reinterpret_cast<const float4*>(poses), M, qa, k_eff, out_idx,
-                     out_dist, reinterpret_cast<float4*>(out_query));
+  const float4* P = reinterpret_cast<const float4*>(poses);
+  float4* oq = reinterpret_cast<float4*>(out_query);
+  if (M <= 64)
+    hipLaunchKernelGGL((pose_topk_kernel<64, 1>), dim3(1), dim3(64), 0, s, P, M, qa, k_eff,
+                       out_idx, out_dist, oq);
+  else if (M <= 1024)
+    hipLaunchKernelGGL((pose_topk_kernel<256, 4>), dim3(1), dim3(256), 0, s, P, M, qa, k_eff,
+                       out_idx, out_dist, oq);
+  else
+    hipLaunchKernelGGL((pose_topk_kernel<1024, 8>), dim3(1), dim3(1024), 0, s, P, M, qa, k_eff,
+                       out_idx, out_dist, oq);
   return hipGetLastError();
 }
 

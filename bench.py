@@ -52,7 +52,13 @@ CONFIGS = {
                       "1000 stored int4 chunks (r=0.5, g32 bf16 scales), extrapolated "
                       "query pose, window sink + 4 retrieved + 2 recent + current"),
 }
-CFG_SEED = {"tiny": 1, "1.3b": 2, "14b": 4, "int4": 5}
+CFG_SEED = {"tiny": 1, "1.3b": 2, "14b": 4, "int4": 5, "sweep": 3}
+# Compression sweep: 60 evicted chunks x 30 layers of the 1.3B-class shape,
+# every keep ratio and redundancy fraction below.
+SWEEP = dict(H=12, D=128, T=880, F=3, units=1800, batch=300, ratios=(0.0, 0.25, 0.5, 1.0),
+             p_red=(0.5, 0.7, 0.9),
+             name="compression sweep: 60 chunks x 30 layers = 1800 units of 3x880 tokens x "
+                  "12 heads x d128, r in {0, 0.25, 0.5, 1}, redundancy in {50, 70, 90}%")
 
 
 def parse():
@@ -60,7 +66,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="1.3b", choices=sorted(CONFIGS))
+    ap.add_argument("--config", default="1.3b", choices=sorted(CONFIGS) + ["sweep"])
     ap.add_argument("--r", type=float, default=None, help="override the keep ratio")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--cpu-rows", type=int, default=512,
@@ -127,6 +133,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if a.config == "sweep":
+        sweep(a, torch, w, S, dev)
+        return
     c = dict(CONFIGS[a.config])
     if a.r is not None:
         c["r"] = a.r
@@ -226,12 +235,17 @@ def main():
         t_asm = [e[2].elapsed_time(e[3]) for e in evs]
         t_att = [e[4 + 2 * j].elapsed_time(e[5 + 2 * j]) for e in evs for j in range(nsteps)]
 
+        copy_gbps = None
         if a.copy_probe:
             src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
             src.fill_(1)
+            ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ce0.record()
             dst.copy_(src)
+            ce1.record()
             torch.cuda.synchronize()
+            copy_gbps = 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
             del src, dst
 
     ms_per_step = wall / a.steps * 1e3
@@ -276,6 +290,7 @@ def main():
             "attention_flop": flops,
             "attention_split_keys": splits,
             "event_step_ms": round(comp_ms + pose_ms + asm_ms + att_ms * nsteps, 4),
+            "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         },
         "roofline": {
             "kernel": "wkv_chunk_attention" + (" (fwd + split merge)" if splits else ""),
@@ -291,6 +306,74 @@ def main():
 
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(a, c, sets[0], bank, poses, qhist, Nq, Nk, Lc)
+    print(json.dumps(rec), flush=True)
+
+
+def sweep(a, torch, w, S, dev):
+    """wkv_compress_chunk over all 1800 units for every (redundancy, r) cell.
+    300 distinct units are resident per redundancy fraction; one step
+    compresses all 1800 units as 6 batched calls over them (each call streams
+    4.9 GB of keys and values, far past the last-level cache)."""
+    c = SWEEP
+    H, D, T, F = c["H"], c["D"], c["T"], c["F"]
+    B, nb = c["batch"], c["units"] // c["batch"]
+    R = H * D * 2
+    stream = torch.cuda.Stream()
+    cells = []
+    with torch.cuda.stream(stream):
+        kin = torch.empty((B, F * T, H, D), dtype=torch.bfloat16, device=dev)
+        vin = torch.empty_like(kin)
+        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T), 16), dtype=torch.uint8,
+                         device=dev)
+        for pi, p_red in enumerate(c["p_red"]):
+            for u in range(B):
+                kin[u], vin[u] = S.chunk_kv(3, u, pi, F, T, H, D, p_red=p_red, device=dev)
+            for r in c["ratios"]:
+                n_keep = w.wkv_keep_count(F, T, r)
+                Lc = T + n_keep
+                ko = torch.empty((B, Lc, H, D), dtype=torch.bfloat16, device=dev)
+                vo = torch.empty_like(ko)
+                ki = torch.empty((B, Lc), dtype=torch.int32, device=dev)
+                N = (F - 1) * T
+                s_read = F * T if 0 < n_keep < N else Lc
+                unit_bytes = R * (s_read + 3 * Lc)
+
+                def step():
+                    for _ in range(nb):
+                        w.wkv_compress_chunk(kin, vin, F, T, r, k_out=ko, v_out=vo,
+                                             kept_idx=ki, ws=ws)
+                for _ in range(max(1, a.warmup // 5)):
+                    step()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = max(1, a.steps // 10)
+                e0.record()
+                for _ in range(reps):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                gbps = unit_bytes * c["units"] / (ms * 1e-3) / 1e9
+                cells.append({"p_red": p_red, "r": r, "ms": round(ms, 3), "GB": round(unit_bytes * c["units"] / 1e9, 2),
+                              "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)})
+                del ko, vo, ki
+    main_cell = next(x for x in cells if x["p_red"] == 0.7 and x["r"] == 0.5)
+    rec = {
+        "metric": METRIC,
+        "value": main_cell["GBps"],
+        "unit": "GB/s (wkv_compress_chunk over 1800 units, algorithmic bytes, r=0.5, 70% redundancy)",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": main_cell["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, f64 scores",
+        "data": "synthetic (seeded rho-mixture keys, N(0,1) values)",
+        "config": {"workload": c["name"], "heads": H, "head_dim": D, "tokens_per_frame": T,
+                   "frames_per_chunk": F, "units": c["units"], "batch": B, "parallelism": "none"},
+        "sweep": cells,
+        "roofline": {"kernel": "wkv_compress_chunk (score + select + gather)", "bound": "hbm",
+                     "achieved": main_cell["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": main_cell["frac"], "traffic": None},
+        "cpu_baseline": None,
+    }
     print(json.dumps(rec), flush=True)
 
 
