@@ -304,6 +304,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
     weights();
+    // Instruction order for this region (sched_group_barrier masks: 0x100 LDS
+    // read, 0x008 MFMA, 0x002 VALU): the first 4 K reads of S^T(t+1) up
+    // front, then each of its 16 MFMAs followed by the next K read and 6 of
+    // the softmax VALU ops of tile t, so MFMAs never wait on a K read that
+    // was just issued and the VALU work is spread between them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
     // Range guard. The reference mref stays where it is while every half-row
     // tile sum is <= 2^30 (no weight near the fp32/bf16 range) and every row
     // has accumulated >= 2^-60 (what dominates it has not underflowed).
@@ -345,6 +362,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[kt][mm], o[dt], 0, 0, 0);
         }
+    // P*V region: each MFMA right after the two transposing reads it needs.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
     sc[0] = sn[0];
     sc[1] = sn[1];
 

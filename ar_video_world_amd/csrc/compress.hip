@@ -17,7 +17,9 @@
 //            (score, index) key, stable compaction by block scan, writes
 //            kept_idx.
 //   gather - one wave per output row: copies the kept K rows (non-anchor) and
-//            all kept V rows with 16-byte loads and stores.
+//            all kept V rows with 16-byte loads and stores. Outputs and V
+//            (read once) use streaming accesses; the kept K rows use the
+//            default policy since the score pass has just read them.
 #include "wkv_common.hpp"
 #include "wkv_internal.hpp"
 #include "wkv_select.hpp"
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-      *reinterpret_cast<uint4*>(kout_unit + aoff + i * 32) = a[i];
+      st_stream(kout_unit + aoff + i * 32, a[i]);
     double na = 0.0;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
@@ -209,14 +211,14 @@ __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
     rd[r] = act ? dst + (size_t)row * cpr : nullptr;
   }
   for (int c = lane; c < cpr; c += 64) {
-    uint4 b0 = rs[0] ? rs[0][c] : make_uint4(0, 0, 0, 0);
-    uint4 b1 = rs[1] ? rs[1][c] : make_uint4(0, 0, 0, 0);
-    uint4 b2 = rs[2] ? rs[2][c] : make_uint4(0, 0, 0, 0);
-    uint4 b3 = rs[3] ? rs[3][c] : make_uint4(0, 0, 0, 0);
-    if (rd[0]) rd[0][c] = b0;
-    if (rd[1]) rd[1][c] = b1;
-    if (rd[2]) rd[2][c] = b2;
-    if (rd[3]) rd[3][c] = b3;
+    uint4 b0 = rs[0] ? (isk ? rs[0][c] : ld_stream(rs[0] + c)) : make_uint4(0, 0, 0, 0);
+    uint4 b1 = rs[1] ? (isk ? rs[1][c] : ld_stream(rs[1] + c)) : make_uint4(0, 0, 0, 0);
+    uint4 b2 = rs[2] ? (isk ? rs[2][c] : ld_stream(rs[2] + c)) : make_uint4(0, 0, 0, 0);
+    uint4 b3 = rs[3] ? (isk ? rs[3][c] : ld_stream(rs[3] + c)) : make_uint4(0, 0, 0, 0);
+    if (rd[0]) st_stream(rd[0] + c, b0);
+    if (rd[1]) st_stream(rd[1] + c, b1);
+    if (rd[2]) st_stream(rd[2] + c, b2);
+    if (rd[3]) st_stream(rd[3] + c, b3);
   }
 }
 
