@@ -33,7 +33,10 @@ reason in the design notes):
 * The compression score compares each non-anchor key with the anchor key at
   the *same token position*, per head, and averages the cosine over heads
   (the paper's equation averages over all anchor tokens; the position-aligned
-  head mean is the form the workload definition fixes).
+  head mean is the form the workload definition fixes). The equation's own
+  form (mean over all T anchor tokens) is the second score mode; its head
+  reduction is the same mean over heads, since the equation is stated for
+  one d-dimensional key per token and the model's keys are per head.
 * The keep ratio r is the fraction of pooled non-anchor tokens retained;
   n_keep = round-half-away(r * (F-1) * T) computed in float64 from r as a
   float32, clamped to [0, (F-1)*T].
@@ -132,6 +135,37 @@ def compress_scores(k_bits, F: int, T: int) -> np.ndarray:
     return s.reshape(-1)
 
 
+def compress_scores_anchor_mean(k_bits, F: int, T: int) -> np.ndarray:
+    """The score exactly as WorldKV Sec. 4.3's equation prints it, float64
+    [(F-1)*T]: for frame f >= 1 and token j, the mean over all T anchor-frame
+    tokens i of the cosine between k[f,j] and k[0,i], per head,
+        c_h = (1/T) * sum_i <k[f,j,h], k[0,i,h]> / sqrt(|k[f,j,h]|^2 * |k[0,i,h]|^2)
+    (a pair with a zero norm contributes 0 and still counts in the 1/T), then
+    averaged over heads as the position-aligned form is: s = (1/H) sum_h c_h.
+    The T x T cosine matrix of each head and frame is formed explicitly.
+    """
+    K = bf16_to_f64(k_bits)
+    FT, H, D = K.shape
+    assert FT == F * T
+    K = K.reshape(F, T, H, D)
+    s = np.zeros((F - 1, T), dtype=np.float64)
+    for h in range(H):
+        A = K[0, :, h, :]                                  # [T(i)][D]
+        na = np.sum(A * A, axis=-1)                        # [T(i)]
+        for f in range(1, F):
+            X = K[f, :, h, :]                              # [T(j)][D]
+            nk = np.sum(X * X, axis=-1)                    # [T(j)]
+            G = np.matmul(X, A.T)                          # [j][i] dot products
+            prod = nk[:, None] * na[None, :]
+            safe = np.where(prod == 0.0, 1.0, prod)
+            cos = np.where(prod == 0.0, 0.0, G / np.sqrt(safe))
+            s[f - 1] += np.sum(cos, axis=1) / T
+    return (s / H).reshape(-1)
+
+
+SCORE_MODES = {"position": compress_scores, "anchor_mean": compress_scores_anchor_mean}
+
+
 def select_kept(scores: np.ndarray, n_keep: int) -> np.ndarray:
     """Pooled indices of the n_keep lowest scores, ascending.
 
@@ -146,19 +180,20 @@ def select_kept(scores: np.ndarray, n_keep: int) -> np.ndarray:
     return np.sort(order[:n_keep])
 
 
-def compress_chunk(k_bits, v_bits, F: int, T: int, r: float):
+def compress_chunk(k_bits, v_bits, F: int, T: int, r: float, score_mode: str = "position"):
     """World Compression of one (chunk, layer) unit.
 
     WorldKV Sec. 4.3: the compressed chunk is every anchor-frame token plus
     the retained tokens. Returns (k_out, v_out, kept_idx, scores) with k_out /
     v_out bf16 bits [T + n_keep][H][D], kept_idx int32 in-chunk source rows
     (anchor rows 0..T-1 then kept rows ascending) and scores float64
-    [(F-1)*T].
+    [(F-1)*T]. score_mode picks the score: "position" (compress_scores) or
+    "anchor_mean" (compress_scores_anchor_mean).
     """
     k_bits = np.asarray(k_bits).view(np.uint16)
     v_bits = np.asarray(v_bits).view(np.uint16)
     n_keep = keep_count(F, T, r)
-    scores = compress_scores(k_bits, F, T)
+    scores = SCORE_MODES[score_mode](k_bits, F, T)
     kept = select_kept(scores, n_keep)
     kept_idx = np.concatenate([np.arange(T), T + kept]).astype(np.int32)
     return k_bits[kept_idx], v_bits[kept_idx], kept_idx, scores
