@@ -37,20 +37,24 @@ wkv_status check_hd(int32_t H, int32_t D) {
   return WKV_OK;
 }
 
-// Compute units of the current device, cached per device id.
-int num_cus() {
+// An attribute of the current device, cached per device id.
+template <hipDeviceAttribute_t ATTR>
+int device_attr(int fallback) {
   static std::mutex mu;
   static int cache[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
   std::lock_guard<std::mutex> lk(mu);
   if (cache[dev] == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (hipDeviceGetAttribute(&n, ATTR, dev) != hipSuccess || n <= 0) n = fallback;
     cache[dev] = n;
   }
   return cache[dev];
 }
+
+int num_cus() { return device_attr<hipDeviceAttributeMultiprocessorCount>(256); }
+int max_lds_per_block() { return device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536); }
 
 int64_t keep_count(int32_t F, int32_t T, float r) {
   const int64_t N = (int64_t)(F - 1) * T;
@@ -60,6 +64,24 @@ int64_t keep_count(int32_t F, int32_t T, float r) {
   if (n < 0) n = 0;
   if (n > N) n = N;
   return n;
+}
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace layout: [scores B*N][anchor-mean partials B*H*slices*D][abar B*H*D],
+// float64, each part 256-byte aligned; the last two for the anchor-mean score.
+struct CompressWsLayout {
+  size_t scores, part, abar, total;
+};
+CompressWsLayout compress_ws_layout(int32_t B, int32_t F, int32_t T, int32_t H, int32_t D,
+                                    bool mean, bool scores_in_ws) {
+  CompressWsLayout L{};
+  L.scores = 0;
+  L.part = scores_in_ws ? round_up((size_t)B * (size_t)(F - 1) * (size_t)T * sizeof(double)) : 0;
+  L.abar = L.part + (mean ? round_up((size_t)B * H * wkv::compress_mean_slices(T) * D * sizeof(double)) : 0);
+  L.total = L.abar + (mean ? round_up((size_t)B * H * D * sizeof(double)) : 0);
+  return L;
 }
 
 }  // namespace
@@ -76,15 +98,17 @@ int32_t wkv_keep_count(int32_t F, int32_t T, float r) {
   return (int32_t)keep_count(F, T, r);
 }
 
-size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T) {
-  if (B < 1 || F < 2 || T < 1) return 0;
-  return (size_t)B * (size_t)(F - 1) * (size_t)T * sizeof(double);
+size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H, int32_t D,
+                                    int32_t score_mode) {
+  if (B < 1 || F < 2 || T < 1 || H < 1 || D < 1) return 0;
+  if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN) return 0;
+  return compress_ws_layout(B, F, T, H, D, score_mode == WKV_SCORE_ANCHOR_MEAN, true).total;
 }
 
 wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
-                              int32_t T, int32_t H, int32_t D, float r, uint16_t* k_out,
-                              uint16_t* v_out, int32_t* kept_idx, double* scores, void* ws,
-                              size_t ws_bytes, wkv_stream_t stream) {
+                              int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
+                              uint16_t* k_out, uint16_t* v_out, int32_t* kept_idx, double* scores,
+                              void* ws, size_t ws_bytes, wkv_stream_t stream) {
   if (!k || !v || !k_out || !v_out || !kept_idx)
     return fail(WKV_ERR_NULL, "wkv_compress_chunk: k, v, k_out, v_out and kept_idx are required");
   if (wkv_status st = check_hd(H, D)) return st;
@@ -96,6 +120,8 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, i
   if ((int64_t)B * F * T * H * D >= ((int64_t)1 << 40))
     return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: batch too large");
   if (!(r >= 0.0f && r <= 1.0f)) return fail(WKV_ERR_RATIO, "wkv_compress_chunk: r=%g not in [0,1]", (double)r);
+  if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN)
+    return fail(WKV_ERR_UNSUPPORTED, "wkv_compress_chunk: score_mode=%d (supported: 0, 1)", score_mode);
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out) ||
       !aligned16(kept_idx) || (scores && !aligned16(scores)) || (ws && !aligned16(ws)))
     return fail(WKV_ERR_ALIGN, "wkv_compress_chunk: device pointers must be 16-byte aligned");
@@ -103,15 +129,19 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, i
   const int N = (F - 1) * T;
   const bool need_scores = scores != nullptr;
   const bool score = need_scores || (n_keep > 0 && n_keep < N);
-  double* sbuf = scores;
-  if (score && !sbuf) {
-    const size_t need = wkv_compress_workspace_bytes(B, F, T);
-    if (!ws || ws_bytes < need)
-      return fail(WKV_ERR_WORKSPACE, "wkv_compress_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
-    sbuf = static_cast<double*>(ws);
-  }
+  const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
+  const CompressWsLayout L = compress_ws_layout(B, F, T, H, D, mean, score && !scores);
+  if (L.total > 0 && (!ws || ws_bytes < L.total))
+    return fail(WKV_ERR_WORKSPACE, "wkv_compress_chunk: workspace %zu bytes < %zu needed",
+                ws ? ws_bytes : (size_t)0, L.total);
+  if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean) > (size_t)max_lds_per_block())
+    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: H*D too large for the score kernel's LDS");
+  char* wsb = static_cast<char*>(ws);
+  double* sbuf = scores ? scores : (score ? reinterpret_cast<double*>(wsb + L.scores) : nullptr);
+  double* part = mean ? reinterpret_cast<double*>(wsb + L.part) : nullptr;
+  double* abar = mean ? reinterpret_cast<double*>(wsb + L.abar) : nullptr;
   hipError_t e = wkv::compress_launch(k, v, B, F, T, H, D, n_keep, k_out, v_out, kept_idx, sbuf,
-                                      need_scores, static_cast<hipStream_t>(stream));
+                                      need_scores, part, abar, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "wkv_compress_chunk launch");
   return WKV_OK;
 }

@@ -12,6 +12,14 @@
 //            per-head cosine in LDS; the block then averages over heads in a
 //            fixed order. The anchor slice already sits in registers, so the
 //            score kernel also writes the anchor rows of k_out.
+//            With the anchor-mean score (the section's equation: the mean
+//            cosine to all T anchor tokens) two kernels run first instead:
+//            anchor-mean sums, per (anchor-token slice, head), the unit
+//            anchor keys k/|k| in float64 and writes those anchor rows of
+//            k_out; a finalize kernel adds the slices in a fixed order and
+//            divides by T. The mean of the cosines to every anchor token
+//            is then one dot product, <k, abar> / |k|, so the score kernel
+//            reads only the non-anchor rows and abar (kept in LDS).
 //   select - one block per unit, sized to the pooled count (256, 512 or 1024
 //            threads, 8 keys each): radix select of the n_keep-th smallest
 //            (score, index) key, stable compaction by block scan, writes
@@ -66,11 +74,106 @@ __device__ __forceinline__ double quad_sum(double x) {
   return x;
 }
 
-// grid: (ceil(T / TT), B). Dynamic LDS: TT * (F-1) * H doubles.
-template <int D, int F>
+// grid: (ceil(T / kMeanTok), H, B). Sum over a slice of anchor tokens of the
+// unit anchor keys of one head (a zero key adds nothing), float64, into
+// part[b][h][slice][D]; copies those anchor rows to k_out. 4 lanes own one
+// row slice of D elements, as in the score kernel.
+constexpr int kMeanTok = 128;
+
+template <int D>
+__global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
+    const uint16_t* __restrict__ k, int F, int T, int H, double* __restrict__ part,
+    uint16_t* __restrict__ k_out, int Lc) {
+  constexpr int NLD = D / 32;
+  constexpr int E = NLD * 8;  // elements per lane
+  __shared__ double red[kScoreBlock / 64][D];
+  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int j0 = sl * kMeanTok;
+  const int ntok = min(kMeanTok, T - j0);
+  const int tid = threadIdx.x;
+  const int slot = tid / kLanesPerPair;
+  const int sub = tid % kLanesPerPair;
+  const size_t HD = (size_t)H * D;
+  const uint16_t* unit = k + (size_t)b * F * T * HD;
+  uint16_t* kout_unit = k_out + (size_t)b * Lc * HD;
+  double acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0;
+  // Every lane of a quad runs the same iterations (quad shuffles inside);
+  // the next token's slice is loaded while this one is reduced.
+  uint4 an[NLD];
+  auto load_row = [&](int jl) {
+    const size_t off = ((size_t)(j0 + jl) * H + h) * D + sub * 8;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) an[i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
+  };
+  if (slot < ntok) load_row(slot);
+  for (int jl = slot; jl < ntok; jl += kPairsPerPass) {
+    const size_t off = ((size_t)(j0 + jl) * H + h) * D + sub * 8;
+    uint4 a[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) a[i] = an[i];
+    if (jl + kPairsPerPass < ntok) load_row(jl + kPairsPerPass);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) st_stream(kout_unit + off + i * 32, a[i]);
+    double na = 0.0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
+    na = quad_sum(na);
+    const double inv = (na == 0.0) ? 0.0 : 1.0 / sqrt(na);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[i * 8 + 2 * q] = fma((double)bf16_to_f32(w[q] & 0xFFFFu), inv, acc[i * 8 + 2 * q]);
+        acc[i * 8 + 2 * q + 1] = fma((double)bf16_to_f32(w[q] >> 16), inv, acc[i * 8 + 2 * q + 1]);
+      }
+    }
+  }
+  // Lanes with the same sub hold the same elements: butterfly over the 16
+  // quads of a wave, then a fixed-order sum over the waves.
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane < kLanesPerPair) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][i * 32 + sub * 8 + e] = acc[i * 8 + e];
+  }
+  __syncthreads();
+  double* dst = part + (((size_t)b * H + h) * gridDim.x + sl) * D;
+  for (int d = tid; d < D; d += kScoreBlock) {
+    double t = red[0][d];
+#pragma unroll
+    for (int w = 1; w < kScoreBlock / 64; ++w) t += red[w][d];
+    dst[d] = t;
+  }
+}
+
+// grid: (H, B), block D. abar[b][h][d] = (sum over slices, in order) / T.
+__global__ void compress_anchor_mean_final_kernel(const double* __restrict__ part, int nslice,
+                                                  int T, int H, double* __restrict__ abar) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, D = blockDim.x;
+  const double* src = part + ((size_t)b * H + h) * nslice * D + d;
+  double t = 0.0;
+  for (int s = 0; s < nslice; ++s) t += src[(size_t)s * D];
+  abar[((size_t)b * H + h) * D + d] = t / (double)T;
+}
+
+// grid: (ceil(T / TT), B). Dynamic LDS: TT * (F-1) * H doubles, then (MEAN)
+// H rows of D + kAbarSkew doubles holding abar.
+constexpr int kAbarSkew = 2;
+
+template <int D, int F, bool MEAN>
 __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
     const uint16_t* __restrict__ k, int T, int H, int TT,
-    double* __restrict__ scores, uint16_t* __restrict__ k_out, int Lc) {
+    double* __restrict__ scores, uint16_t* __restrict__ k_out, int Lc,
+    const double* __restrict__ abar_g) {
   constexpr int NLD = D / 32;  // 16-byte loads per lane per row slice
   extern __shared__ double cosbuf[];
   const int b = blockIdx.y;
@@ -84,43 +187,118 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
   const uint16_t* unit = k + (size_t)b * F * T * HD;
   uint16_t* kout_unit = k_out + (size_t)b * Lc * HD;
 
-  // Every lane of a quad runs the same number of iterations, so the quad
-  // shuffles below always see their partners.
-  for (int pair = slot; pair < npairs; pair += kPairsPerPass) {
-    const int jl = pair / H;
-    const int h = pair - jl * H;
-    const int j = j0 + jl;
-    uint4 a[NLD];
+  if constexpr (MEAN) {
+    // abar rows sit kAbarSkew doubles apart beyond D, so the quads of a
+    // wave (consecutive heads) read distinct LDS banks.
+    double* abar = cosbuf + (size_t)TT * (F - 1) * H;
     uint4 x[F - 1][NLD];
-    const size_t aoff = ((size_t)j * H + h) * D + sub * 8;
+    auto load_rows = [&](int pr) {
+      const int jl = pr / H;
+      const int h = pr - jl * H;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(unit + aoff + i * 32);
+      for (int f = 1; f < F; ++f) {
+        const size_t off = (((size_t)f * T + j0 + jl) * H + h) * D + sub * 8;
 #pragma unroll
-    for (int f = 1; f < F; ++f) {
-      const size_t off = (((size_t)f * T + j) * H + h) * D + sub * 8;
+        for (int i = 0; i < NLD; ++i)
+          x[f - 1][i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
+      }
+    };
+    // The first rows are in flight while abar is staged.
+    if (slot < npairs) load_rows(slot);
+    const double* src = abar_g + (size_t)b * HD;
+    for (int i = tid; i < (int)HD; i += kScoreBlock)
+      abar[(i / D) * (D + kAbarSkew) + i % D] = src[i];
+    __syncthreads();
+    // Every lane of a quad runs the same number of iterations (quad shuffles).
+    for (int pair = slot; pair < npairs; pair += kPairsPerPass) {
+      const int jl = pair / H;
+      const int h = pair - jl * H;
+      double av[NLD * 8];
+      const double* ah = abar + h * (D + kAbarSkew) + sub * 8;
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
-        x[f - 1][i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[i * 8 + e] = ah[i * 32 + e];
+      uint4 xc[F - 1][NLD];
+#pragma unroll
+      for (int f = 0; f < F - 1; ++f)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) xc[f][i] = x[f][i];
+      if (pair + kPairsPerPass < npairs) load_rows(pair + kPairsPerPass);  // next rows
+#pragma unroll
+      for (int f = 1; f < F; ++f) {
+        double dt = 0.0, nk = 0.0;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const uint32_t w[4] = {xc[f - 1][i].x, xc[f - 1][i].y, xc[f - 1][i].z, xc[f - 1][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double xl = (double)bf16_to_f32(w[q] & 0xFFFFu);
+            const double xh = (double)bf16_to_f32(w[q] >> 16);
+            nk = fma(xl, xl, nk);
+            nk = fma(xh, xh, nk);
+            dt = fma(xl, av[i * 8 + 2 * q], dt);
+            dt = fma(xh, av[i * 8 + 2 * q + 1], dt);
+          }
+        }
+        dt = quad_sum(dt);
+        nk = quad_sum(nk);
+        if (sub == 0) cosbuf[(jl * (F - 1) + (f - 1)) * H + h] = (nk == 0.0) ? 0.0 : dt / sqrt(nk);
+      }
     }
+  } else {
+    // Rows of the next pair are loaded while this pair is reduced.
+    uint4 a[NLD];
+    uint4 x[F - 1][NLD];
+    auto load_rows = [&](int pr) {
+      const int jl = pr / H;
+      const int h = pr - jl * H;
+      const int j = j0 + jl;
+      const size_t aoff = ((size_t)j * H + h) * D + sub * 8;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      st_stream(kout_unit + aoff + i * 32, a[i]);
-    double na = 0.0;
+      for (int i = 0; i < NLD; ++i) a[i] = *reinterpret_cast<const uint4*>(unit + aoff + i * 32);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
-    na = quad_sum(na);
+      for (int f = 1; f < F; ++f) {
+        const size_t off = (((size_t)f * T + j) * H + h) * D + sub * 8;
 #pragma unroll
-    for (int f = 1; f < F; ++f) {
-      double dt = 0.0, nk = 0.0;
+        for (int i = 0; i < NLD; ++i)
+          x[f - 1][i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
+      }
+    };
+    if (slot < npairs) load_rows(slot);
+    // Every lane of a quad runs the same number of iterations, so the quad
+    // shuffles below always see their partners.
+    for (int pair = slot; pair < npairs; pair += kPairsPerPass) {
+      const int jl = pair / H;
+      const int h = pair - jl * H;
+      const size_t aoff = ((size_t)(j0 + jl) * H + h) * D + sub * 8;
+      uint4 ac[NLD];
+      uint4 xc[F - 1][NLD];
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) accum_dot_sq(x[f - 1][i], a[i], dt, nk);
-      dt = quad_sum(dt);
-      nk = quad_sum(nk);
-      if (sub == 0) {
-        const double prod = nk * na;
-        const double c = (prod == 0.0) ? 0.0 : dt / sqrt(prod);
-        cosbuf[(jl * (F - 1) + (f - 1)) * H + h] = c;
+      for (int i = 0; i < NLD; ++i) ac[i] = a[i];
+#pragma unroll
+      for (int f = 0; f < F - 1; ++f)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) xc[f][i] = x[f][i];
+      if (pair + kPairsPerPass < npairs) load_rows(pair + kPairsPerPass);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) st_stream(kout_unit + aoff + i * 32, ac[i]);
+      double na = 0.0;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) accum_sq(ac[i], na);
+      na = quad_sum(na);
+#pragma unroll
+      for (int f = 1; f < F; ++f) {
+        double dt = 0.0, nk = 0.0;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) accum_dot_sq(xc[f - 1][i], ac[i], dt, nk);
+        dt = quad_sum(dt);
+        nk = quad_sum(nk);
+        if (sub == 0) {
+          const double prod = nk * na;
+          const double c = (prod == 0.0) ? 0.0 : dt / sqrt(prod);
+          cosbuf[(jl * (F - 1) + (f - 1)) * H + h] = c;
+        }
       }
     }
   }
@@ -223,22 +401,29 @@ __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
 }
 
 template <int D, int F>
-hipError_t launch_score(const uint16_t* k, int B, int T, int H, int TT,
-                        double* scores, uint16_t* k_out, int Lc, hipStream_t s) {
+hipError_t launch_score(const uint16_t* k, int B, int T, int H, int TT, double* scores,
+                        uint16_t* k_out, int Lc, const double* abar, hipStream_t s) {
   dim3 grid((T + TT - 1) / TT, B);
   size_t lds = (size_t)TT * (F - 1) * H * sizeof(double);
-  hipLaunchKernelGGL((compress_score_kernel<D, F>), grid, dim3(kScoreBlock), lds, s,
-                     k, T, H, TT, scores, k_out, Lc);
+  if (abar) {
+    lds += (size_t)H * (D + kAbarSkew) * sizeof(double);
+    hipLaunchKernelGGL((compress_score_kernel<D, F, true>), grid, dim3(kScoreBlock), lds, s,
+                       k, T, H, TT, scores, k_out, Lc, abar);
+  } else {
+    hipLaunchKernelGGL((compress_score_kernel<D, F, false>), grid, dim3(kScoreBlock), lds, s,
+                       k, T, H, TT, scores, k_out, Lc, abar);
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_score_F(const uint16_t* k, int B, int F, int T, int H, int TT,
-                            double* scores, uint16_t* k_out, int Lc, hipStream_t s) {
+                            double* scores, uint16_t* k_out, int Lc, const double* abar,
+                            hipStream_t s) {
   switch (F) {
-    case 2: return launch_score<D, 2>(k, B, T, H, TT, scores, k_out, Lc, s);
-    case 3: return launch_score<D, 3>(k, B, T, H, TT, scores, k_out, Lc, s);
-    case 4: return launch_score<D, 4>(k, B, T, H, TT, scores, k_out, Lc, s);
+    case 2: return launch_score<D, 2>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
+    case 3: return launch_score<D, 3>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
+    case 4: return launch_score<D, 4>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -255,19 +440,40 @@ int compress_score_tile(int B, int T, int H) {
   return tt < T ? tt : T;
 }
 
+int compress_mean_slices(int T) { return (T + kMeanTok - 1) / kMeanTok; }
+
+size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean) {
+  const int TT = compress_score_tile(B, T, H);
+  return ((size_t)TT * (F - 1) * H + (mean ? (size_t)H * (D + kAbarSkew) : 0)) * sizeof(double);
+}
+
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                            int T, int H, int D, int n_keep, uint16_t* k_out,
                            uint16_t* v_out, int32_t* kept_idx, double* scores,
-                           bool need_scores, hipStream_t s) {
+                           bool need_scores, double* mean_part, double* abar,
+                           hipStream_t s) {
   const int N = (F - 1) * T;
   const int Lc = T + n_keep;
   const int cpr = H * D / 8;
   const bool score = need_scores || (n_keep > 0 && n_keep < N);
   hipError_t e = hipSuccess;
   if (score) {
+    if (abar) {
+      const int ns = compress_mean_slices(T);
+      if (D == 128)
+        hipLaunchKernelGGL(compress_anchor_mean_kernel<128>, dim3(ns, H, B), dim3(kScoreBlock), 0,
+                           s, k, F, T, H, mean_part, k_out, Lc);
+      else
+        hipLaunchKernelGGL(compress_anchor_mean_kernel<64>, dim3(ns, H, B), dim3(kScoreBlock), 0,
+                           s, k, F, T, H, mean_part, k_out, Lc);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(compress_anchor_mean_final_kernel, dim3(H, B), dim3(D), 0, s,
+                         mean_part, ns, T, H, abar);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int TT = compress_score_tile(B, T, H);
-    e = (D == 128) ? dispatch_score_F<128>(k, B, F, T, H, TT, scores, k_out, Lc, s)
-                   : dispatch_score_F<64>(k, B, F, T, H, TT, scores, k_out, Lc, s);
+    e = (D == 128) ? dispatch_score_F<128>(k, B, F, T, H, TT, scores, k_out, Lc, abar, s)
+                   : dispatch_score_F<64>(k, B, F, T, H, TT, scores, k_out, Lc, abar, s);
     if (e != hipSuccess) return e;
   }
   if (N <= 256 * kSelKPT)

@@ -12,10 +12,15 @@ constexpr int kMaxSegments = 16;  // sink + up to 14 recent + current
 
 // ---- compression
 int compress_score_tile(int B, int T, int H);
+int compress_mean_slices(int T);  // anchor-token slices of the anchor-mean sums
+size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean);
+// mean_part [B][H][slices][D] and abar [B][H][D] (float64) are used, and must
+// be given, for the anchor-mean score only; abar == nullptr selects the
+// position-aligned score.
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, int T,
                            int H, int D, int n_keep, uint16_t* k_out, uint16_t* v_out,
                            int32_t* kept_idx, double* scores, bool need_scores,
-                           hipStream_t s);
+                           double* mean_part, double* abar, hipStream_t s);
 
 // ---- pose top-k
 hipError_t pose_topk_launch(const void* poses, int M, const float* last,

@@ -65,9 +65,9 @@ def _sig(name, res, args):
 _abi_version = _sig("wkv_abi_version", _I32, [])
 _last_error = _sig("wkv_last_error", C.c_char_p, [])
 _keep_count = _sig("wkv_keep_count", _I32, [_I32, _I32, _F])
-_compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32, _I32, _I32])
+_compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 6)
 _compress = _sig("wkv_compress_chunk", C.c_int,
-                 [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P])
+                 [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _SZ, _P])
 _pose_topk = _sig("wkv_pose_topk", C.c_int,
                   [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P, _P, _P])
 _assemble = _sig("wkv_assemble_window", C.c_int,
@@ -121,8 +121,18 @@ def wkv_keep_count(F: int, T: int, r: float) -> int:
     return int(_keep_count(F, T, r))
 
 
-def wkv_compress_workspace_bytes(B: int, F: int, T: int) -> int:
-    return int(_compress_ws(B, F, T))
+WKV_SCORE_POSITION = 0
+WKV_SCORE_ANCHOR_MEAN = 1
+_SCORE_MODES = {"position": WKV_SCORE_POSITION, "anchor_mean": WKV_SCORE_ANCHOR_MEAN}
+
+
+def _score_mode(mode) -> int:
+    return _SCORE_MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def wkv_compress_workspace_bytes(B: int, F: int, T: int, H: int, D: int,
+                                 score_mode="position") -> int:
+    return int(_compress_ws(B, F, T, H, D, _score_mode(score_mode)))
 
 
 def wkv_attention_workspace_bytes(Nq: int, Nk: int, H: int, D: int) -> int:
@@ -131,8 +141,10 @@ def wkv_attention_workspace_bytes(Nq: int, Nk: int, H: int, D: int) -> int:
 
 def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
                        k_out=None, v_out=None, kept_idx=None, scores=None,
-                       want_scores: bool = False, ws=None, stream=None):
+                       want_scores: bool = False, ws=None, stream=None,
+                       score_mode="position"):
     """World Compression of B units. k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]).
+    score_mode: "position" / "anchor_mean" (or the WKV_SCORE_* value).
     Returns (k_out, v_out, kept_idx, scores-or-None)."""
     _bits(k, "k"), _bits(v, "v")
     squeeze = k.dim() == 3
@@ -153,9 +165,10 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     if scores is None and want_scores:
         scores = torch.empty((B, (F - 1) * T), dtype=torch.float64, device=dev)
     if ws is None:
-        nb = wkv_compress_workspace_bytes(B, F, T)
+        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
-    st = _compress(_ptr(k), _ptr(v), B, F, T, H, D, r, _ptr(k_out), _ptr(v_out),
+    st = _compress(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
+                   _ptr(k_out), _ptr(v_out),
                    _ptr(kept_idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
     _check("wkv_compress_chunk", st)
     if squeeze:

@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="1.3b", choices=sorted(CONFIGS) + ["sweep"])
     ap.add_argument("--r", type=float, default=None, help="override the keep ratio")
+    ap.add_argument("--score-mode", default="position", choices=["position", "anchor_mean"],
+                    help="compression score: cosine to the anchor key at the same position "
+                         "(default) or the mean cosine to every anchor key")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows per oracle attention call in the CPU baseline")
@@ -182,7 +185,7 @@ def main():
                 wk=torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev),
                 wv=torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)))
-        cws = torch.empty(max(w.wkv_compress_workspace_bytes(1, F, T), 16),
+        cws = torch.empty(max(w.wkv_compress_workspace_bytes(1, F, T, H, D, "anchor_mean"), 16),
                           dtype=torch.uint8, device=dev)
         aws = torch.empty(max(w.wkv_attention_workspace_bytes(Nq, Nk, H, D), 16),
                           dtype=torch.uint8, device=dev)
@@ -193,7 +196,7 @@ def main():
             if ev is not None:
                 ev[0].record()
             w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
-                                 kept_idx=s["kidx"], ws=cws)
+                                 kept_idx=s["kidx"], ws=cws, score_mode=a.score_mode)
             if ev is not None:
                 ev[1].record()
             idx, _, _ = w.wkv_pose_topk(poses, qhist, k, want_dist=False)
@@ -235,6 +238,21 @@ def main():
         t_asm = [e[2].elapsed_time(e[3]) for e in evs]
         t_att = [e[4 + 2 * j].elapsed_time(e[5 + 2 * j]) for e in evs for j in range(nsteps)]
 
+        # ---- compression alone under each score mode (event-timed, same sets)
+        comp_modes = {}
+        for mode in ("position", "anchor_mean"):
+            cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+            for i in range(25):
+                s = sets[i % len(sets)]
+                if i >= 5:
+                    cev[i - 5][0].record()
+                w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                     kept_idx=s["kidx"], ws=cws, score_mode=mode)
+                if i >= 5:
+                    cev[i - 5][1].record()
+            torch.cuda.synchronize()
+            comp_modes[mode] = statistics.fmean(e[0].elapsed_time(e[1]) for e in cev)
+
         copy_gbps = None
         if a.copy_probe:
             src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -273,7 +291,8 @@ def main():
         "data": "synthetic (seeded rho-mixture keys, N(0,1) values and queries, "
                 "random-walk poses)",
         "config": {"workload": c["name"], "heads": H, "head_dim": D, "tokens_per_frame": T,
-                   "frames_per_chunk": F, "keep_ratio": r, "compressed_rows": Lc,
+                   "frames_per_chunk": F, "keep_ratio": r, "score_mode": a.score_mode,
+                   "compressed_rows": Lc,
                    "stored_chunks": M, "retrieved": k, "window_keys": Nk, "queries": Nq,
                    "denoise_steps": nsteps, "int4_bank": c["int4"], "parallelism": "none",
                    "input_sets": a.sets},
@@ -281,6 +300,9 @@ def main():
             "compress_us": round(comp_ms * 1e3, 2),
             "compress_GBps": round(comp_b / (comp_ms * 1e-3) / 1e9, 1),
             "compress_bytes": comp_b,
+            "compress_score_modes": {m: {"us": round(v * 1e3, 2),
+                                         "GBps": round(comp_b / (v * 1e-3) / 1e9, 1)}
+                                     for m, v in comp_modes.items()},
             "pose_topk_us": round(pose_ms * 1e3, 2),
             "assemble_us": round(asm_ms * 1e3, 2),
             "assemble_GBps": round(asm_b / (asm_ms * 1e-3) / 1e9, 1),
@@ -323,8 +345,8 @@ def sweep(a, torch, w, S, dev):
     with torch.cuda.stream(stream):
         kin = torch.empty((B, F * T, H, D), dtype=torch.bfloat16, device=dev)
         vin = torch.empty_like(kin)
-        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T), 16), dtype=torch.uint8,
-                         device=dev)
+        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T, H, D, a.score_mode), 16),
+                         dtype=torch.uint8, device=dev)
         for pi, p_red in enumerate(c["p_red"]):
             for u in range(B):
                 kin[u], vin[u] = S.chunk_kv(3, u, pi, F, T, H, D, p_red=p_red, device=dev)
@@ -341,7 +363,7 @@ def sweep(a, torch, w, S, dev):
                 def step():
                     for _ in range(nb):
                         w.wkv_compress_chunk(kin, vin, F, T, r, k_out=ko, v_out=vo,
-                                             kept_idx=ki, ws=ws)
+                                             kept_idx=ki, ws=ws, score_mode=a.score_mode)
                 for _ in range(max(1, a.warmup // 5)):
                     step()
                 torch.cuda.synchronize()
@@ -367,7 +389,8 @@ def sweep(a, torch, w, S, dev):
         "vs_baseline": None, "dtype": "bf16 in, f64 scores",
         "data": "synthetic (seeded rho-mixture keys, N(0,1) values)",
         "config": {"workload": c["name"], "heads": H, "head_dim": D, "tokens_per_frame": T,
-                   "frames_per_chunk": F, "units": c["units"], "batch": B, "parallelism": "none"},
+                   "frames_per_chunk": F, "units": c["units"], "batch": B,
+                   "score_mode": a.score_mode, "parallelism": "none"},
         "sweep": cells,
         "roofline": {"kernel": "wkv_compress_chunk (score + select + gather)", "bound": "hbm",
                      "achieved": main_cell["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -392,7 +415,7 @@ def cpu_baseline(a, c, s, bank, poses, qhist, Nq, Nk, Lc):
     ek, ev = bits(s["ek"]), bits(s["ev"])
     P = poses.cpu().numpy()
     t0 = time.perf_counter()
-    O.compress_chunk(ek, ev, F, T, r)
+    O.compress_chunk(ek, ev, F, T, r, score_mode=a.score_mode)
     t1 = time.perf_counter()
     if len(qhist) == 2:
         q = O.pose_extrapolate(np.asarray(qhist[0], np.float32), np.asarray(qhist[1], np.float32))

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define WKV_ABI_VERSION 1
+#define WKV_ABI_VERSION 2
 
 typedef void* wkv_stream_t; /* hipStream_t */
 
@@ -101,9 +101,14 @@ const char* wkv_last_error(void);
  *
  * A unit is one evicted chunk at one layer: F frames x T tokens, frame 0 is
  * the anchor. For every non-anchor token (frame f >= 1, position j) the score
- *     s[(f-1)*T + j] = (1/H) * sum_h cos(K[f,j,h,:], K[0,j,h,:])
- * is the head-mean cosine to the anchor key at the same position (0 when a
- * norm is 0), computed in float64. The n_keep = wkv_keep_count(F, T, r)
+ * is, in float64, with cos = 0 when a norm is 0:
+ *   WKV_SCORE_POSITION     s[(f-1)*T + j] = (1/H) sum_h cos(K[f,j,h,:], K[0,j,h,:])
+ *                          the head-mean cosine to the anchor key at the same
+ *                          position;
+ *   WKV_SCORE_ANCHOR_MEAN  s[(f-1)*T + j] = (1/H) sum_h (1/T) sum_i cos(K[f,j,h,:], K[0,i,h,:])
+ *                          the section's equation as printed: the mean cosine
+ *                          to every anchor-frame key, averaged over heads.
+ * The n_keep = wkv_keep_count(F, T, r)
  * lowest (score, pooled index) pairs are retained (ties go to the lower
  * index, NaN orders last). The compressed unit is the T anchor rows followed
  * by the retained rows in ascending source order, for K and V alike.
@@ -114,8 +119,13 @@ const char* wkv_last_error(void);
  * are T + n_keep. */
 int32_t wkv_keep_count(int32_t F, int32_t T, float r);
 
-/* [host] Workspace bytes wkv_compress_chunk needs for B units. */
-size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T);
+enum { WKV_SCORE_POSITION = 0, WKV_SCORE_ANCHOR_MEAN = 1 };
+
+/* [host] Workspace bytes wkv_compress_chunk needs for B units with the given
+ * score mode (an upper bound: a call that is given its scores output, or
+ * that needs no score at r = 0 or 1, uses less). 0 for invalid arguments. */
+size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H,
+                                    int32_t D, int32_t score_mode);
 
 /* Compress B contiguous units.
  *   k, v       bf16 [B][F*T][H][D]            inputs
@@ -123,13 +133,15 @@ size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T);
  *   v_out      bf16 [B][Lc][H][D]             outputs, Lc = T + n_keep
  *   kept_idx   int32 [B][Lc]                  output: in-unit source row of
  *                                             every output row, ascending
+ *   score_mode WKV_SCORE_POSITION or WKV_SCORE_ANCHOR_MEAN
  *   scores     double [B][(F-1)*T] or NULL    optional output
- *   ws         >= wkv_compress_workspace_bytes(B, F, T) bytes (may be NULL
- *              when that is 0)
- * Limits: 1 <= B; 2 <= F <= 8; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1. */
+ *   ws         >= wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
+ *              bytes (may be NULL when that is 0)
+ * Limits: 1 <= B; 2 <= F <= 4; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1.
+ * Errors: WKV_ERR_UNSUPPORTED for an unknown score_mode. */
 wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
                               int32_t F, int32_t T, int32_t H, int32_t D,
-                              float r, uint16_t* k_out, uint16_t* v_out,
+                              float r, int32_t score_mode, uint16_t* k_out, uint16_t* v_out,
                               int32_t* kept_idx, double* scores, void* ws,
                               size_t ws_bytes, wkv_stream_t stream);
 

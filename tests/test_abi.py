@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(w):
 
 
 def test_abi_version_and_keep_count(w):
-    assert w.wkv_abi_version() == 1
+    assert w.wkv_abi_version() == 2
     assert w.wkv_keep_count(3, 880, 0.5) == 880
     assert w.wkv_keep_count(3, 880, 0.25) == 440
     assert w.wkv_keep_count(3, 1560, 0.25) == 780
@@ -47,7 +47,11 @@ def test_abi_version_and_keep_count(w):
     assert w.wkv_keep_count(3, 7, float("nan")) == -1
     assert w.wkv_keep_count(3, 7, 1.5) == -1
     assert w.wkv_keep_count(1, 7, 0.5) == -1
-    assert w.wkv_compress_workspace_bytes(4, 3, 880) == 4 * 1760 * 8
+    assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128) == 4 * 1760 * 8
+    # anchor-mean: + partial sums [B][H][ceil(T/128)][D] + abar [B][H][D], float64
+    assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, "anchor_mean") == \
+        4 * 1760 * 8 + 4 * 12 * 7 * 128 * 8 + 4 * 12 * 128 * 8
+    assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, 2) == 0
     assert w.wkv_attention_workspace_bytes(0, 1, 1, 128) == 0
 
 
@@ -69,11 +73,12 @@ def st(fn, *args):
 
 def test_compress_validation(w):
     f = w._compress
-    ok = [A, A, 1, 3, 64, 2, 64, 0.5, A, A, A, None, A, 1 << 20, None]
+    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, None, A, 1 << 20, None]
 
     def call(**kw):
         a = list(ok)
-        names = ["k", "v", "B", "F", "T", "H", "D", "r", "ko", "vo", "ki", "sc", "ws", "wsb", "s"]
+        names = ["k", "v", "B", "F", "T", "H", "D", "r", "mode", "ko", "vo", "ki", "sc", "ws",
+                 "wsb", "s"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return f(*a)
@@ -95,6 +100,11 @@ def test_compress_validation(w):
     assert call(ws=None, wsb=0) == 6
     assert call(wsb=100) == 6
     assert "workspace" in w.wkv_last_error()
+    assert call(mode=2) == 7
+    assert call(mode=-1) == 7
+    # anchor-mean needs room for its partial sums even when scores are given
+    assert call(mode=1, sc=A, ws=None, wsb=0) == 6
+    assert call(mode=1, wsb=w.wkv_compress_workspace_bytes(1, 3, 64, 2, 64, "anchor_mean") - 1) == 6
 
 
 def test_pose_validation(w):

@@ -22,13 +22,13 @@ def w():
     return w
 
 
-def run_case(w, K, V, F, T, r, label, want_scores=True, report=None):
+def run_case(w, K, V, F, T, r, label, want_scores=True, report=None, score_mode="position"):
     """K, V: CPU bf16 [B, F*T, H, D]. Compares every unit with the oracle."""
     B = K.shape[0]
     dev = torch.device("cuda:0")
-    say("compress", label, tuple(K.shape), "r", r)
+    say("compress", label, tuple(K.shape), "r", r, score_mode)
     ko, vo, ki, sc = w.wkv_compress_chunk(K.to(dev), V.to(dev), F, T, r,
-                                          want_scores=want_scores)
+                                          want_scores=want_scores, score_mode=score_mode)
     torch.cuda.synchronize()
     ko, vo, ki = np_bits(ko), np_bits(vo), ki.cpu().numpy()
     sc = sc.cpu().numpy() if sc is not None else None
@@ -36,7 +36,7 @@ def run_case(w, K, V, F, T, r, label, want_scores=True, report=None):
     bands = []
     for b in range(B):
         kb, vb = np_bits(K[b]), np_bits(V[b])
-        ok, ov, oi, os_ = O.compress_chunk(kb, vb, F, T, r)
+        ok, ov, oi, os_ = O.compress_chunk(kb, vb, F, T, r, score_mode=score_mode)
         if sc is not None:
             both_nan = np.isnan(os_) & np.isnan(sc[b])
             d = np.where(both_nan, 0.0, np.abs(sc[b] - os_))
