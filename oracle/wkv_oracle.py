@@ -290,8 +290,10 @@ def int4_quantize(x_bits):
     """bf16 rows -> (packed uint8 [..., D/2], scale bf16 bits [..., D/32]).
 
     Symmetric per-32 group: scale = bf16_RNE(float32(max|x|) / 7 in float32),
-    q = clamp(rint(x / scale in float32), -8, 7), q = 0 when the scale is 0.
-    (Harness-side encoder used to build test banks; not on the hot path.)
+    q = clamp(rint(x / scale in float32), -8, 7), q = 0 when the scale is 0
+    (rint rounds half to even; both divisions are correctly rounded float32).
+    Inputs are finite. Used to build test banks and, through
+    compress_chunk_int4, as the definition of the quantise-on-store output.
     """
     x = bf16_to_f64(x_bits).astype(np.float32)
     shp = x.shape
@@ -306,6 +308,18 @@ def int4_quantize(x_bits):
     u = (q & 0x0F).astype(np.uint8)
     packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
     return packed, sbits
+
+
+def compress_chunk_int4(k_bits, v_bits, F: int, T: int, r: float, score_mode: str = "position"):
+    """World Compression whose output is stored in the int4 bank format
+    (WorldPager abstract / Fig. 2: the KV store holds int4 blocks): the
+    compressed rows of compress_chunk, each quantised by int4_quantize.
+    Returns (k_packed, v_packed, k_scale_bits, v_scale_bits, kept_idx, scores).
+    """
+    ko, vo, kept_idx, scores = compress_chunk(k_bits, v_bits, F, T, r, score_mode)
+    kp, ks = int4_quantize(ko)
+    vp, vs = int4_quantize(vo)
+    return kp, vp, ks, vs, kept_idx, scores
 
 
 # ----------------------------------------------------------------------------

@@ -176,3 +176,67 @@ def test_window_layout_and_offsets():
     assert np.array_equal(wk[4:10], bank[0][1]) and np.array_equal(wv[10:16], bank[1][4])
     assert np.array_equal(wk[16:19], recent[0][0]) and np.array_equal(wv[19:24], recent[1][1])
     assert np.array_equal(wv[24:], cur[1])
+
+
+# ---------------------------------------------------------------- int4 encoder
+
+def _group(vals, D=32):
+    x = np.zeros((1, D), dtype=np.float32)
+    x[0, :len(vals)] = vals
+    return O.f32_to_bf16_rne(x)
+
+
+def _codes(packed):
+    b = np.asarray(packed, dtype=np.uint8)
+    q = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int32)
+    q[..., 0::2] = b & 0x0F
+    q[..., 1::2] = b >> 4
+    return np.where(q >= 8, q - 16, q)
+
+
+def test_int4_scale_is_bf16_of_amax_over_7_by_hand():
+    # amax = 1: 1/7 = 1.001001001...b x 2^-3; bf16 keeps 7 fraction bits,
+    # 1.0010010|01001... rounds down -> 73/512 = 0.142578125.
+    packed, sb = O.int4_quantize(_group([1.0, 0.5, -0.5, 0.25, -1.0]))
+    assert O.bf16_to_f64(sb)[0, 0] == 73 / 512
+    # x / s in float32: 1/s = 7.0137 -> 7; 0.5/s = 3.5068 -> 4; 0.25/s = 1.7534 -> 2
+    assert list(_codes(packed)[0, :5]) == [7, 4, -4, 2, -7]
+    assert np.all(_codes(packed)[0, 5:] == 0)
+
+
+def test_int4_ties_round_to_even_and_zero_group():
+    # amax = 7 -> scale exactly 1: x/s = x, ties go to the even code
+    packed, sb = O.int4_quantize(_group([7.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -6.5]))
+    assert O.bf16_to_f64(sb)[0, 0] == 1.0
+    assert list(_codes(packed)[0, :8]) == [7, 2, 4, -2, 0, 0, 2, -6]
+    packed, sb = O.int4_quantize(_group([]))
+    assert sb[0, 0] == 0 and np.all(packed == 0)
+
+
+def test_int4_groups_are_independent_and_row_major():
+    # two groups of one row: each takes its own scale
+    x = np.zeros((1, 64), dtype=np.float32)
+    x[0, 0] = 7.0          # group 0: scale 1
+    x[0, 33] = 14.0        # group 1: scale 2, code of 14 is 7 at element 33
+    packed, sb = O.int4_quantize(O.f32_to_bf16_rne(x))
+    assert list(O.bf16_to_f64(sb)[0]) == [1.0, 2.0]
+    q = _codes(packed)[0]
+    assert q[0] == 7 and q[33] == 7 and np.count_nonzero(q) == 2
+    assert packed[0, 16] == 0x70          # element 33 is the high nibble of byte 16
+
+
+def test_compress_chunk_int4_is_compress_then_quantise():
+    rng = np.random.default_rng(6)
+    F, T, H, D = 3, 16, 2, 64
+    kb = O.f32_to_bf16_rne(rng.standard_normal((F * T, H, D)).astype(np.float32))
+    vb = O.f32_to_bf16_rne(rng.standard_normal((F * T, H, D)).astype(np.float32))
+    kp, vp, ks, vs, ki, sc = O.compress_chunk_int4(kb, vb, F, T, 0.25)
+    ko, vo, ki2, _ = O.compress_chunk(kb, vb, F, T, 0.25)
+    assert np.array_equal(ki, ki2)
+    assert kp.shape == (T + 8, H, D // 2) and ks.shape == (T + 8, H, D // 32)
+    # dequantised output within the encoder's error bound of the bf16 rows
+    for p, sb, ref in ((kp, ks, ko), (vp, vs, vo)):
+        xr = O.bf16_to_f64(O.int4_dequant(p, sb))
+        xs = O.bf16_to_f64(ref)
+        s = np.repeat(O.bf16_to_f64(sb), 32, axis=-1)
+        assert np.all(np.abs(xr - xs) <= 0.5 * s * (1 + 2 ** -7) + np.abs(xr) * 2 ** -8 + 1e-30)
