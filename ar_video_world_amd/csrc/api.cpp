@@ -84,6 +84,48 @@ CompressWsLayout compress_ws_layout(int32_t B, int32_t F, int32_t T, int32_t H, 
   return L;
 }
 
+// Validation and launch shared by the bf16 and int4 compression entry points
+// (their output pointers are checked by the callers).
+wkv_status compress_common(const char* fn, const uint16_t* k, const uint16_t* v, int32_t B,
+                           int32_t F, int32_t T, int32_t H, int32_t D, float r,
+                           int32_t score_mode, const wkv::CompressDst& dst, int32_t* kept_idx,
+                           double* scores, void* ws, size_t ws_bytes, wkv_stream_t stream) {
+  if (!k || !v || !kept_idx)
+    return fail(WKV_ERR_NULL, "%s: k, v and kept_idx are required", fn);
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (B < 1 || F < 2 || F > 4 || T < 1)
+    return fail(WKV_ERR_SHAPE, "%s: need B>=1, 2<=F<=4, T>=1 (B=%d F=%d T=%d)", fn, B, F, T);
+  if ((int64_t)(F - 1) * T > 8192)
+    return fail(WKV_ERR_SHAPE, "%s: (F-1)*T=%lld exceeds 8192", fn, (long long)(F - 1) * T);
+  if ((int64_t)B * F * T * H * D >= ((int64_t)1 << 40))
+    return fail(WKV_ERR_SHAPE, "%s: batch too large", fn);
+  if (!(r >= 0.0f && r <= 1.0f)) return fail(WKV_ERR_RATIO, "%s: r=%g not in [0,1]", fn, (double)r);
+  if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: score_mode=%d (supported: 0, 1)", fn, score_mode);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kept_idx) || (scores && !aligned16(scores)) ||
+      (ws && !aligned16(ws)))
+    return fail(WKV_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+  const int n_keep = (int)keep_count(F, T, r);
+  const int N = (F - 1) * T;
+  const bool need_scores = scores != nullptr;
+  const bool score = need_scores || (n_keep > 0 && n_keep < N);
+  const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
+  const CompressWsLayout L = compress_ws_layout(B, F, T, H, D, mean, score && !scores);
+  if (L.total > 0 && (!ws || ws_bytes < L.total))
+    return fail(WKV_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn,
+                ws ? ws_bytes : (size_t)0, L.total);
+  if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean) > (size_t)max_lds_per_block())
+    return fail(WKV_ERR_SHAPE, "%s: H*D too large for the score kernel's LDS", fn);
+  char* wsb = static_cast<char*>(ws);
+  double* sbuf = scores ? scores : (score ? reinterpret_cast<double*>(wsb + L.scores) : nullptr);
+  double* part = mean ? reinterpret_cast<double*>(wsb + L.part) : nullptr;
+  double* abar = mean ? reinterpret_cast<double*>(wsb + L.abar) : nullptr;
+  hipError_t e = wkv::compress_launch(k, v, B, F, T, H, D, n_keep, dst, kept_idx, sbuf,
+                                      need_scores, part, abar, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return WKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,41 +151,29 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, i
                               int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
                               uint16_t* k_out, uint16_t* v_out, int32_t* kept_idx, double* scores,
                               void* ws, size_t ws_bytes, wkv_stream_t stream) {
-  if (!k || !v || !k_out || !v_out || !kept_idx)
+  if (!k_out || !v_out)
     return fail(WKV_ERR_NULL, "wkv_compress_chunk: k, v, k_out, v_out and kept_idx are required");
-  if (wkv_status st = check_hd(H, D)) return st;
-  if (B < 1 || F < 2 || F > 4 || T < 1)
-    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: need B>=1, 2<=F<=4, T>=1 (B=%d F=%d T=%d)", B, F, T);
-  if ((int64_t)(F - 1) * T > 8192)
-    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: (F-1)*T=%lld exceeds 8192",
-                (long long)(F - 1) * T);
-  if ((int64_t)B * F * T * H * D >= ((int64_t)1 << 40))
-    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: batch too large");
-  if (!(r >= 0.0f && r <= 1.0f)) return fail(WKV_ERR_RATIO, "wkv_compress_chunk: r=%g not in [0,1]", (double)r);
-  if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN)
-    return fail(WKV_ERR_UNSUPPORTED, "wkv_compress_chunk: score_mode=%d (supported: 0, 1)", score_mode);
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out) ||
-      !aligned16(kept_idx) || (scores && !aligned16(scores)) || (ws && !aligned16(ws)))
+  if (!aligned16(k_out) || !aligned16(v_out))
     return fail(WKV_ERR_ALIGN, "wkv_compress_chunk: device pointers must be 16-byte aligned");
-  const int n_keep = (int)keep_count(F, T, r);
-  const int N = (F - 1) * T;
-  const bool need_scores = scores != nullptr;
-  const bool score = need_scores || (n_keep > 0 && n_keep < N);
-  const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
-  const CompressWsLayout L = compress_ws_layout(B, F, T, H, D, mean, score && !scores);
-  if (L.total > 0 && (!ws || ws_bytes < L.total))
-    return fail(WKV_ERR_WORKSPACE, "wkv_compress_chunk: workspace %zu bytes < %zu needed",
-                ws ? ws_bytes : (size_t)0, L.total);
-  if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean) > (size_t)max_lds_per_block())
-    return fail(WKV_ERR_SHAPE, "wkv_compress_chunk: H*D too large for the score kernel's LDS");
-  char* wsb = static_cast<char*>(ws);
-  double* sbuf = scores ? scores : (score ? reinterpret_cast<double*>(wsb + L.scores) : nullptr);
-  double* part = mean ? reinterpret_cast<double*>(wsb + L.part) : nullptr;
-  double* abar = mean ? reinterpret_cast<double*>(wsb + L.abar) : nullptr;
-  hipError_t e = wkv::compress_launch(k, v, B, F, T, H, D, n_keep, k_out, v_out, kept_idx, sbuf,
-                                      need_scores, part, abar, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "wkv_compress_chunk launch");
-  return WKV_OK;
+  return compress_common("wkv_compress_chunk", k, v, B, F, T, H, D, r, score_mode,
+                         wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
+                         kept_idx, scores, ws, ws_bytes, stream);
+}
+
+wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
+                                   int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
+                                   uint8_t* k_packed, uint8_t* v_packed, uint16_t* k_scale,
+                                   uint16_t* v_scale, int32_t* kept_idx, double* scores, void* ws,
+                                   size_t ws_bytes, wkv_stream_t stream) {
+  if (!k_packed || !v_packed || !k_scale || !v_scale)
+    return fail(WKV_ERR_NULL,
+                "wkv_compress_chunk_int4: k, v, k_packed, v_packed, k_scale, v_scale and kept_idx "
+                "are required");
+  if (!aligned16(k_packed) || !aligned16(v_packed) || !aligned16(k_scale) || !aligned16(v_scale))
+    return fail(WKV_ERR_ALIGN, "wkv_compress_chunk_int4: device pointers must be 16-byte aligned");
+  return compress_common("wkv_compress_chunk_int4", k, v, B, F, T, H, D, r, score_mode,
+                         wkv::CompressDst{nullptr, nullptr, k_packed, v_packed, k_scale, v_scale},
+                         kept_idx, scores, ws, ws_bytes, stream);
 }
 
 wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M, const wkv_pose* query_hist,

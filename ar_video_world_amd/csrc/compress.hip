@@ -74,16 +74,99 @@ __device__ __forceinline__ double quad_sum(double x) {
   return x;
 }
 
+// int4 encoding of one 32-element group held by the 4 lanes of a quad, 8
+// consecutive elements per lane in lane order: scale = bf16_RNE(max|x| / 7),
+// code = clamp(rint(x / scale), -8, 7), or 0 when the scale is 0; both
+// divisions are correctly rounded float32 and rint rounds half to even.
+// Returns this lane's 4 bytes (element e in bits 4e..4e+3, so the low
+// nibble of each byte holds the even element); *sbits gets the scale.
+__device__ __forceinline__ uint32_t int4_encode_quad(const uint4& x, uint16_t* sbits) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf16_to_f32(w[q] & 0xFFFFu);
+    v[2 * q + 1] = bf16_to_f32(w[q] >> 16);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const uint16_t sb = f32_to_bf16(__fdiv_rn(m, 7.0f));
+  const float sc = bf16_to_f32(sb);
+  uint32_t out = 0;
+  if (sc != 0.f) {
+    // x and sc carry 8-bit significands, so an exact quotient x / sc that is
+    // not a half-integer lies at least 1/1020 from one: the correctly
+    // rounded float32 quotient and x * rcp(sc) (error < 2e-6 for |x/sc| <= 8)
+    // round to the same integer. Exact half-integers are told apart by the
+    // exact residual x - q*sc (q has 4 bits, so the fma is exact) and moved
+    // to the even neighbour. A scale so small that rcp overflows takes the
+    // division.
+    const float inv = __builtin_amdgcn_rcpf(sc);
+    float q[8];
+    if (inv < 3.0e38f) {
+      const float hs = 0.5f * sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qa = rintf(v[e] * inv);
+        const float r = fmaf(-qa, sc, v[e]);
+        const bool tie_odd = (fabsf(r) == hs) & (((int)qa & 1) != 0);
+        q[e] = tie_odd ? qa + copysignf(1.f, r) : qa;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = rintf(__fdiv_rn(v[e], sc));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out |= ((uint32_t)(int)fminf(fmaxf(q[e], -8.f), 7.f) & 0xFu) << (4 * e);
+  }
+  *sbits = sb;
+  return out;
+}
+
+// Where compressed rows go: bf16 rows, or int4 codes + bf16 group scales.
+struct CompressOut {
+  uint16_t* k;     // bf16 [B][Lc][H][D]
+  uint16_t* v;
+  uint8_t* kq;     // int4 [B][Lc][H][D/2]
+  uint8_t* vq;
+  uint16_t* ks;    // bf16 [B][Lc][H][D/32]
+  uint16_t* vs;
+};
+
+// Stores the (row, head) slice a quad holds (lane `sub` has 16-byte pieces
+// i at elements sub*8 + i*32) at element offset `e0` = (row*H + h)*D of a
+// unit's output, as bf16 or int4.
+template <int NLD, bool Q4>
+__device__ __forceinline__ void store_slice(const uint4 (&a)[NLD], size_t e0, int sub,
+                                            uint16_t* bf, uint8_t* pk, uint16_t* sc) {
+  if constexpr (!Q4) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) st_stream(bf + e0 + sub * 8 + i * 32, a[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      uint16_t sb;
+      const uint32_t p = int4_encode_quad(a[i], &sb);
+      *reinterpret_cast<uint32_t*>(pk + e0 / 2 + i * 16 + sub * 4) = p;
+      if (sub == 0) sc[e0 / 32 + i] = sb;
+    }
+  }
+}
+
 // grid: (ceil(T / kMeanTok), H, B). Sum over a slice of anchor tokens of the
 // unit anchor keys of one head (a zero key adds nothing), float64, into
 // part[b][h][slice][D]; copies those anchor rows to k_out. 4 lanes own one
 // row slice of D elements, as in the score kernel.
 constexpr int kMeanTok = 128;
 
-template <int D>
+template <int D, bool Q4>
 __global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
     const uint16_t* __restrict__ k, int F, int T, int H, double* __restrict__ part,
-    uint16_t* __restrict__ k_out, int Lc) {
+    CompressOut out, int Lc) {
   constexpr int NLD = D / 32;
   constexpr int E = NLD * 8;  // elements per lane
   __shared__ double red[kScoreBlock / 64][D];
@@ -95,7 +178,7 @@ __global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
   const int sub = tid % kLanesPerPair;
   const size_t HD = (size_t)H * D;
   const uint16_t* unit = k + (size_t)b * F * T * HD;
-  uint16_t* kout_unit = k_out + (size_t)b * Lc * HD;
+  const size_t ubase = (size_t)b * Lc * HD;  // element offset of this unit's output
   double acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0;
@@ -109,13 +192,11 @@ __global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
   };
   if (slot < ntok) load_row(slot);
   for (int jl = slot; jl < ntok; jl += kPairsPerPass) {
-    const size_t off = ((size_t)(j0 + jl) * H + h) * D + sub * 8;
     uint4 a[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) a[i] = an[i];
     if (jl + kPairsPerPass < ntok) load_row(jl + kPairsPerPass);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) st_stream(kout_unit + off + i * 32, a[i]);
+    store_slice<NLD, Q4>(a, ubase + ((size_t)(j0 + jl) * H + h) * D, sub, out.k, out.kq, out.ks);
     double na = 0.0;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
@@ -169,10 +250,10 @@ __global__ void compress_anchor_mean_final_kernel(const double* __restrict__ par
 // H rows of D + kAbarSkew doubles holding abar.
 constexpr int kAbarSkew = 2;
 
-template <int D, int F, bool MEAN>
+template <int D, int F, bool MEAN, bool Q4>
 __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
     const uint16_t* __restrict__ k, int T, int H, int TT,
-    double* __restrict__ scores, uint16_t* __restrict__ k_out, int Lc,
+    double* __restrict__ scores, CompressOut out, int Lc,
     const double* __restrict__ abar_g) {
   constexpr int NLD = D / 32;  // 16-byte loads per lane per row slice
   extern __shared__ double cosbuf[];
@@ -185,7 +266,7 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
   const int sub = tid % kLanesPerPair;
   const size_t HD = (size_t)H * D;
   const uint16_t* unit = k + (size_t)b * F * T * HD;
-  uint16_t* kout_unit = k_out + (size_t)b * Lc * HD;
+  const size_t ubase = (size_t)b * Lc * HD;  // element offset of this unit's output
 
   if constexpr (MEAN) {
     // abar rows sit kAbarSkew doubles apart beyond D, so the quads of a
@@ -271,7 +352,6 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
     for (int pair = slot; pair < npairs; pair += kPairsPerPass) {
       const int jl = pair / H;
       const int h = pair - jl * H;
-      const size_t aoff = ((size_t)(j0 + jl) * H + h) * D + sub * 8;
       uint4 ac[NLD];
       uint4 xc[F - 1][NLD];
 #pragma unroll
@@ -281,8 +361,8 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
 #pragma unroll
         for (int i = 0; i < NLD; ++i) xc[f][i] = x[f][i];
       if (pair + kPairsPerPass < npairs) load_rows(pair + kPairsPerPass);
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) st_stream(kout_unit + aoff + i * 32, ac[i]);
+      store_slice<NLD, Q4>(ac, ubase + ((size_t)(j0 + jl) * H + h) * D, sub, out.k, out.kq,
+                           out.ks);
       double na = 0.0;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) accum_sq(ac[i], na);
@@ -364,15 +444,16 @@ constexpr int kRowsPerWave = 4;  // the copy loop below is written for 4
 
 // grid: (ceil(Lc / (waves * kRowsPerWave)), B, 2). z = 0 copies K rows (rows
 // below k_skip are skipped: the score kernel already wrote them), z = 1
-// copies V rows. cpr = 16-byte chunks per row.
+// copies V rows. cpr = 16-byte chunks (8 elements) per row; with int4
+// output the 4 lanes holding one 32-element group encode it together.
+template <bool Q4>
 __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kept_idx, int FT, int Lc, int cpr, int k_skip,
-    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
+    CompressOut out) {
   const int b = blockIdx.y;
   const bool isk = blockIdx.z == 0;
   const uint4* src = reinterpret_cast<const uint4*>(isk ? k : v) + (size_t)b * FT * cpr;
-  uint4* dst = reinterpret_cast<uint4*>(isk ? k_out : v_out) + (size_t)b * Lc * cpr;
   const int32_t* idx = kept_idx + (size_t)b * Lc;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -380,52 +461,78 @@ __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
   const int lo = isk ? k_skip : 0;
   // Resolve each row's source once (wave-uniform), then stream its columns.
   const uint4* rs[kRowsPerWave];
-  uint4* rd[kRowsPerWave];
+  size_t ro[kRowsPerWave];   // output row (chunk units), or ~0 when inactive
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int row = row0 + r;
     const bool act = row < Lc && row >= lo;
     rs[r] = act ? src + (size_t)idx[row] * cpr : nullptr;
-    rd[r] = act ? dst + (size_t)row * cpr : nullptr;
+    ro[r] = act ? ((size_t)b * Lc + row) * cpr : ~(size_t)0;
   }
   for (int c = lane; c < cpr; c += 64) {
-    uint4 b0 = rs[0] ? (isk ? rs[0][c] : ld_stream(rs[0] + c)) : make_uint4(0, 0, 0, 0);
-    uint4 b1 = rs[1] ? (isk ? rs[1][c] : ld_stream(rs[1] + c)) : make_uint4(0, 0, 0, 0);
-    uint4 b2 = rs[2] ? (isk ? rs[2][c] : ld_stream(rs[2] + c)) : make_uint4(0, 0, 0, 0);
-    uint4 b3 = rs[3] ? (isk ? rs[3][c] : ld_stream(rs[3] + c)) : make_uint4(0, 0, 0, 0);
-    if (rd[0]) st_stream(rd[0] + c, b0);
-    if (rd[1]) st_stream(rd[1] + c, b1);
-    if (rd[2]) st_stream(rd[2] + c, b2);
-    if (rd[3]) st_stream(rd[3] + c, b3);
+    uint4 x[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r)
+      x[r] = rs[r] ? (isk ? rs[r][c] : ld_stream(rs[r] + c)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      if constexpr (!Q4) {
+        if (ro[r] != ~(size_t)0)
+          st_stream(reinterpret_cast<uint4*>(isk ? out.k : out.v) + ro[r] + c, x[r]);
+      } else {
+        uint16_t sb;
+        const uint32_t p = int4_encode_quad(x[r], &sb);   // every lane of the quad
+        if (ro[r] != ~(size_t)0) {
+          reinterpret_cast<uint32_t*>(isk ? out.kq : out.vq)[ro[r] + c] = p;
+          if ((c & 3) == 0) (isk ? out.ks : out.vs)[(ro[r] + c) / 4] = sb;
+        }
+      }
+    }
   }
 }
 
 template <int D, int F>
 hipError_t launch_score(const uint16_t* k, int B, int T, int H, int TT, double* scores,
-                        uint16_t* k_out, int Lc, const double* abar, hipStream_t s) {
+                        const CompressOut& out, bool q4, int Lc, const double* abar,
+                        hipStream_t s) {
   dim3 grid((T + TT - 1) / TT, B);
   size_t lds = (size_t)TT * (F - 1) * H * sizeof(double);
-  if (abar) {
+  if (abar) {  // the anchor-mean kernel has stored the anchor rows
     lds += (size_t)H * (D + kAbarSkew) * sizeof(double);
-    hipLaunchKernelGGL((compress_score_kernel<D, F, true>), grid, dim3(kScoreBlock), lds, s,
-                       k, T, H, TT, scores, k_out, Lc, abar);
+    hipLaunchKernelGGL((compress_score_kernel<D, F, true, false>), grid, dim3(kScoreBlock), lds,
+                       s, k, T, H, TT, scores, out, Lc, abar);
+  } else if (q4) {
+    hipLaunchKernelGGL((compress_score_kernel<D, F, false, true>), grid, dim3(kScoreBlock), lds,
+                       s, k, T, H, TT, scores, out, Lc, abar);
   } else {
-    hipLaunchKernelGGL((compress_score_kernel<D, F, false>), grid, dim3(kScoreBlock), lds, s,
-                       k, T, H, TT, scores, k_out, Lc, abar);
+    hipLaunchKernelGGL((compress_score_kernel<D, F, false, false>), grid, dim3(kScoreBlock),
+                       lds, s, k, T, H, TT, scores, out, Lc, abar);
   }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_score_F(const uint16_t* k, int B, int F, int T, int H, int TT,
-                            double* scores, uint16_t* k_out, int Lc, const double* abar,
-                            hipStream_t s) {
+                            double* scores, const CompressOut& out, bool q4, int Lc,
+                            const double* abar, hipStream_t s) {
   switch (F) {
-    case 2: return launch_score<D, 2>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
-    case 3: return launch_score<D, 3>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
-    case 4: return launch_score<D, 4>(k, B, T, H, TT, scores, k_out, Lc, abar, s);
+    case 2: return launch_score<D, 2>(k, B, T, H, TT, scores, out, q4, Lc, abar, s);
+    case 3: return launch_score<D, 3>(k, B, T, H, TT, scores, out, q4, Lc, abar, s);
+    case 4: return launch_score<D, 4>(k, B, T, H, TT, scores, out, q4, Lc, abar, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D>
+void launch_anchor_mean(const uint16_t* k, int B, int F, int T, int H, double* part,
+                        const CompressOut& out, bool q4, int Lc, hipStream_t s) {
+  const dim3 grid(compress_mean_slices(T), H, B);
+  if (q4)
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true>), grid, dim3(kScoreBlock), 0, s, k,
+                       F, T, H, part, out, Lc);
+  else
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, false>), grid, dim3(kScoreBlock), 0, s,
+                       k, F, T, H, part, out, Lc);
 }
 
 }  // namespace
@@ -448,10 +555,11 @@ size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean) {
 }
 
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
-                           int T, int H, int D, int n_keep, uint16_t* k_out,
-                           uint16_t* v_out, int32_t* kept_idx, double* scores,
-                           bool need_scores, double* mean_part, double* abar,
-                           hipStream_t s) {
+                           int T, int H, int D, int n_keep, const CompressDst& dst,
+                           int32_t* kept_idx, double* scores, bool need_scores,
+                           double* mean_part, double* abar, hipStream_t s) {
+  const bool q4 = dst.k_packed != nullptr;
+  const CompressOut out{dst.k, dst.v, dst.k_packed, dst.v_packed, dst.k_scale, dst.v_scale};
   const int N = (F - 1) * T;
   const int Lc = T + n_keep;
   const int cpr = H * D / 8;
@@ -461,19 +569,17 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
     if (abar) {
       const int ns = compress_mean_slices(T);
       if (D == 128)
-        hipLaunchKernelGGL(compress_anchor_mean_kernel<128>, dim3(ns, H, B), dim3(kScoreBlock), 0,
-                           s, k, F, T, H, mean_part, k_out, Lc);
+        launch_anchor_mean<128>(k, B, F, T, H, mean_part, out, q4, Lc, s);
       else
-        hipLaunchKernelGGL(compress_anchor_mean_kernel<64>, dim3(ns, H, B), dim3(kScoreBlock), 0,
-                           s, k, F, T, H, mean_part, k_out, Lc);
+        launch_anchor_mean<64>(k, B, F, T, H, mean_part, out, q4, Lc, s);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hipLaunchKernelGGL(compress_anchor_mean_final_kernel, dim3(H, B), dim3(D), 0, s,
                          mean_part, ns, T, H, abar);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int TT = compress_score_tile(B, T, H);
-    e = (D == 128) ? dispatch_score_F<128>(k, B, F, T, H, TT, scores, k_out, Lc, abar, s)
-                   : dispatch_score_F<64>(k, B, F, T, H, TT, scores, k_out, Lc, abar, s);
+    e = (D == 128) ? dispatch_score_F<128>(k, B, F, T, H, TT, scores, out, q4, Lc, abar, s)
+                   : dispatch_score_F<64>(k, B, F, T, H, TT, scores, out, q4, Lc, abar, s);
     if (e != hipSuccess) return e;
   }
   if (N <= 256 * kSelKPT)
@@ -489,8 +595,12 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
   if (e != hipSuccess) return e;
   const int rows_per_block = (kGatherBlock / 64) * kRowsPerWave;
   dim3 grid((Lc + rows_per_block - 1) / rows_per_block, B, 2);
-  hipLaunchKernelGGL(compress_gather_kernel, grid, dim3(kGatherBlock), 0, s, k, v,
-                     kept_idx, F * T, Lc, cpr, score ? T : 0, k_out, v_out);
+  if (q4)
+    hipLaunchKernelGGL(compress_gather_kernel<true>, grid, dim3(kGatherBlock), 0, s, k, v,
+                       kept_idx, F * T, Lc, cpr, score ? T : 0, out);
+  else
+    hipLaunchKernelGGL(compress_gather_kernel<false>, grid, dim3(kGatherBlock), 0, s, k, v,
+                       kept_idx, F * T, Lc, cpr, score ? T : 0, out);
   return hipGetLastError();
 }
 

@@ -14,11 +14,22 @@ constexpr int kMaxSegments = 16;  // sink + up to 14 recent + current
 int compress_score_tile(int B, int T, int H);
 int compress_mean_slices(int T);  // anchor-token slices of the anchor-mean sums
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean);
+// Destination of the compressed rows: bf16 rows (k, v) when k_packed is
+// null, else int4 codes (k_packed, v_packed: [B][Lc][H][D/2]) with bf16 group
+// scales (k_scale, v_scale: [B][Lc][H][D/32]).
+struct CompressDst {
+  uint16_t* k;
+  uint16_t* v;
+  uint8_t* k_packed;
+  uint8_t* v_packed;
+  uint16_t* k_scale;
+  uint16_t* v_scale;
+};
 // mean_part [B][H][slices][D] and abar [B][H][D] (float64) are used, and must
 // be given, for the anchor-mean score only; abar == nullptr selects the
 // position-aligned score.
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, int T,
-                           int H, int D, int n_keep, uint16_t* k_out, uint16_t* v_out,
+                           int H, int D, int n_keep, const CompressDst& dst,
                            int32_t* kept_idx, double* scores, bool need_scores,
                            double* mean_part, double* abar, hipStream_t s);
 

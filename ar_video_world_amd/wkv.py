@@ -68,6 +68,9 @@ _keep_count = _sig("wkv_keep_count", _I32, [_I32, _I32, _F])
 _compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 6)
 _compress = _sig("wkv_compress_chunk", C.c_int,
                  [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _SZ, _P])
+_compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
+                  [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
+                   _SZ, _P])
 _pose_topk = _sig("wkv_pose_topk", C.c_int,
                   [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P, _P, _P])
 _assemble = _sig("wkv_assemble_window", C.c_int,
@@ -79,7 +82,8 @@ _attn = _sig("wkv_chunk_attention", C.c_int,
              [_P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P])
 
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
-           "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_pose_topk",
+           "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
+           "wkv_pose_topk",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
 
 
@@ -175,6 +179,49 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
         k_out, v_out, kept_idx = k_out[0], v_out[0], kept_idx[0]
         scores = None if scores is None else scores[0]
     return k_out, v_out, kept_idx, scores
+
+
+def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
+                            k_packed=None, v_packed=None, k_scale=None, v_scale=None,
+                            kept_idx=None, scores=None, want_scores: bool = False, ws=None,
+                            stream=None, score_mode="position"):
+    """World Compression of B units, stored as int4 groups with bf16 scales.
+    k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]). Returns (k_packed, v_packed,
+    k_scale, v_scale, kept_idx, scores-or-None): uint8 [B, Lc, H, D/2] and
+    bf16 [B, Lc, H, D/32]."""
+    _bits(k, "k"), _bits(v, "v")
+    squeeze = k.dim() == 3
+    if squeeze:
+        k, v = k.unsqueeze(0), v.unsqueeze(0)
+    B, FT, H, D = k.shape
+    if FT != F * T:
+        raise ValueError(f"k has {FT} rows per unit, expected F*T={F * T}")
+    Lc = T + max(wkv_keep_count(F, T, r), 0)
+    dev = k.device
+    if k_packed is None:
+        k_packed = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
+    if v_packed is None:
+        v_packed = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
+    if k_scale is None:
+        k_scale = torch.empty((B, Lc, H, D // 32), dtype=torch.bfloat16, device=dev)
+    if v_scale is None:
+        v_scale = torch.empty((B, Lc, H, D // 32), dtype=torch.bfloat16, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, Lc), dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((B, (F - 1) * T), dtype=torch.float64, device=dev)
+    if ws is None:
+        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    st = _compress4(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
+                    _ptr(k_packed), _ptr(v_packed), _ptr(k_scale), _ptr(v_scale),
+                    _ptr(kept_idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
+    _check("wkv_compress_chunk_int4", st)
+    outs = [k_packed, v_packed, k_scale, v_scale, kept_idx]
+    if squeeze:
+        outs = [t[0] for t in outs]
+        scores = None if scores is None else scores[0]
+    return (*outs, scores)
 
 
 def _pose_tuple(p) -> wkv_pose:

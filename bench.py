@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--score-mode", default="position", choices=["position", "anchor_mean"],
                     help="compression score: cosine to the anchor key at the same position "
                          "(default) or the mean cosine to every anchor key")
+    ap.add_argument("--store", default="bf16", choices=["bf16", "int4"],
+                    help="format of the compressed rows in the sweep")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows per oracle attention call in the CPU baseline")
@@ -102,12 +104,22 @@ def measured_traffic(cfg):
     return int(rec["attention_call_bytes"])
 
 
-def algorithmic_bytes(c, Lc, n_keep, Nk):
-    """Bytes the method must move (per call): compress and assemble."""
+def compress_bytes(c, Lc, n_keep, int4=False):
+    """Bytes one compression unit must move: the keys it scores (all F*T
+    rows when a selection is needed, else the Lc kept ones), the kept values,
+    and the Lc compressed K and V rows written (bf16, or int4 codes + bf16
+    scale per 32 elements)."""
     R = c["H"] * c["D"] * 2
     N = (c["F"] - 1) * c["T"]
     s_read = c["F"] * c["T"] if 0 < n_keep < N else Lc
-    comp = R * (s_read + Lc + 2 * Lc)
+    out_row = (c["H"] * c["D"] // 2 + c["H"] * c["D"] // 32 * 2) if int4 else R
+    return R * (s_read + Lc) + 2 * Lc * out_row
+
+
+def algorithmic_bytes(c, Lc, n_keep, Nk):
+    """Bytes the method must move (per call): compress and assemble."""
+    R = c["H"] * c["D"] * 2
+    comp = compress_bytes(c, Lc, n_keep)
     ret_rows = c["k"] * Lc
     other_rows = Nk - ret_rows
     if c["int4"]:
@@ -238,20 +250,34 @@ def main():
         t_asm = [e[2].elapsed_time(e[3]) for e in evs]
         t_att = [e[4 + 2 * j].elapsed_time(e[5 + 2 * j]) for e in evs for j in range(nsteps)]
 
-        # ---- compression alone under each score mode (event-timed, same sets)
+        # ---- compression alone under each score mode and output format
+        # (event-timed, same rotating sets)
+        q4 = [(torch.empty((Lc, H, D // 2), dtype=torch.uint8, device=dev),
+               torch.empty((Lc, H, D // 2), dtype=torch.uint8, device=dev),
+               torch.empty((Lc, H, D // 32), dtype=torch.bfloat16, device=dev),
+               torch.empty((Lc, H, D // 32), dtype=torch.bfloat16, device=dev))
+              for _ in sets]
         comp_modes = {}
-        for mode in ("position", "anchor_mean"):
+        for mode, fmt in (("position", "bf16"), ("anchor_mean", "bf16"), ("position", "int4"),
+                          ("anchor_mean", "int4")):
             cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
             for i in range(25):
                 s = sets[i % len(sets)]
                 if i >= 5:
                     cev[i - 5][0].record()
-                w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
-                                     kept_idx=s["kidx"], ws=cws, score_mode=mode)
+                if fmt == "bf16":
+                    w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                         kept_idx=s["kidx"], ws=cws, score_mode=mode)
+                else:
+                    kp, vp, ks, vs = q4[i % len(sets)]
+                    w.wkv_compress_chunk_int4(s["ek"], s["ev"], F, T, r, k_packed=kp, v_packed=vp,
+                                              k_scale=ks, v_scale=vs, kept_idx=s["kidx"],
+                                              ws=cws, score_mode=mode)
                 if i >= 5:
                     cev[i - 5][1].record()
             torch.cuda.synchronize()
-            comp_modes[mode] = statistics.fmean(e[0].elapsed_time(e[1]) for e in cev)
+            comp_modes[f"{mode}/{fmt}"] = statistics.fmean(e[0].elapsed_time(e[1]) for e in cev)
+        del q4
 
         copy_gbps = None
         if a.copy_probe:
@@ -300,9 +326,11 @@ def main():
             "compress_us": round(comp_ms * 1e3, 2),
             "compress_GBps": round(comp_b / (comp_ms * 1e-3) / 1e9, 1),
             "compress_bytes": comp_b,
-            "compress_score_modes": {m: {"us": round(v * 1e3, 2),
-                                         "GBps": round(comp_b / (v * 1e-3) / 1e9, 1)}
-                                     for m, v in comp_modes.items()},
+            "compress_modes": {m: {"us": round(v * 1e3, 2),
+                                   "bytes": compress_bytes(c, Lc, n_keep, m.endswith("int4")),
+                                   "GBps": round(compress_bytes(c, Lc, n_keep, m.endswith("int4"))
+                                                 / (v * 1e-3) / 1e9, 1)}
+                               for m, v in comp_modes.items()},
             "pose_topk_us": round(pose_ms * 1e3, 2),
             "assemble_us": round(asm_ms * 1e3, 2),
             "assemble_GBps": round(asm_b / (asm_ms * 1e-3) / 1e9, 1),
@@ -339,7 +367,6 @@ def sweep(a, torch, w, S, dev):
     c = SWEEP
     H, D, T, F = c["H"], c["D"], c["T"], c["F"]
     B, nb = c["batch"], c["units"] // c["batch"]
-    R = H * D * 2
     stream = torch.cuda.Stream()
     cells = []
     with torch.cuda.stream(stream):
@@ -353,17 +380,26 @@ def sweep(a, torch, w, S, dev):
             for r in c["ratios"]:
                 n_keep = w.wkv_keep_count(F, T, r)
                 Lc = T + n_keep
-                ko = torch.empty((B, Lc, H, D), dtype=torch.bfloat16, device=dev)
-                vo = torch.empty_like(ko)
                 ki = torch.empty((B, Lc), dtype=torch.int32, device=dev)
-                N = (F - 1) * T
-                s_read = F * T if 0 < n_keep < N else Lc
-                unit_bytes = R * (s_read + 3 * Lc)
+                if a.store == "int4":
+                    ko = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
+                    vo = torch.empty_like(ko)
+                    ks = torch.empty((B, Lc, H, D // 32), dtype=torch.bfloat16, device=dev)
+                    vs = torch.empty_like(ks)
+                else:
+                    ko = torch.empty((B, Lc, H, D), dtype=torch.bfloat16, device=dev)
+                    vo = torch.empty_like(ko)
+                unit_bytes = compress_bytes(c, Lc, n_keep, a.store == "int4")
 
                 def step():
                     for _ in range(nb):
-                        w.wkv_compress_chunk(kin, vin, F, T, r, k_out=ko, v_out=vo,
-                                             kept_idx=ki, ws=ws, score_mode=a.score_mode)
+                        if a.store == "int4":
+                            w.wkv_compress_chunk_int4(kin, vin, F, T, r, k_packed=ko, v_packed=vo,
+                                                      k_scale=ks, v_scale=vs, kept_idx=ki, ws=ws,
+                                                      score_mode=a.score_mode)
+                        else:
+                            w.wkv_compress_chunk(kin, vin, F, T, r, k_out=ko, v_out=vo,
+                                                 kept_idx=ki, ws=ws, score_mode=a.score_mode)
                 for _ in range(max(1, a.warmup // 5)):
                     step()
                 torch.cuda.synchronize()
@@ -379,6 +415,8 @@ def sweep(a, torch, w, S, dev):
                 cells.append({"p_red": p_red, "r": r, "ms": round(ms, 3), "GB": round(unit_bytes * c["units"] / 1e9, 2),
                               "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)})
                 del ko, vo, ki
+                if a.store == "int4":
+                    del ks, vs
     main_cell = next(x for x in cells if x["p_red"] == 0.7 and x["r"] == 0.5)
     rec = {
         "metric": METRIC,
@@ -390,7 +428,7 @@ def sweep(a, torch, w, S, dev):
         "data": "synthetic (seeded rho-mixture keys, N(0,1) values)",
         "config": {"workload": c["name"], "heads": H, "head_dim": D, "tokens_per_frame": T,
                    "frames_per_chunk": F, "units": c["units"], "batch": B,
-                   "score_mode": a.score_mode, "parallelism": "none"},
+                   "score_mode": a.score_mode, "store": a.store, "parallelism": "none"},
         "sweep": cells,
         "roofline": {"kernel": "wkv_compress_chunk (score + select + gather)", "bound": "hbm",
                      "achieved": main_cell["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -145,6 +145,28 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
                               int32_t* kept_idx, double* scores, void* ws,
                               size_t ws_bytes, wkv_stream_t stream);
 
+/* Compress B contiguous units and store the compressed rows in the int4
+ * format of the bank (wkv_bank with WKV_BANK_INT4_G32): the int4 KV store of
+ * [WorldPager] (abstract, Fig. 2) written at eviction time. Selection and
+ * kept_idx / scores are exactly those of wkv_compress_chunk; every output row
+ * is then encoded per group of 32 consecutive elements of one (row, head):
+ *     scale = bf16_RNE(max|x| / 7)      (float32 division, correctly rounded)
+ *     q     = clamp(rint(x / scale), -8, 7), q = 0 when scale == 0
+ * with rint rounding half to even; element d is the low nibble of byte d/2
+ * when d is even, the high nibble when d is odd.
+ *   k_packed,
+ *   v_packed   uint8 [B][Lc][H][D/2]           outputs
+ *   k_scale,
+ *   v_scale    bf16  [B][Lc][H][D/32]          outputs
+ * Other arguments, limits and errors as wkv_compress_chunk. Inputs must be
+ * finite: the codes of a group holding an Inf or NaN are unspecified. */
+wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t B,
+                                   int32_t F, int32_t T, int32_t H, int32_t D, float r,
+                                   int32_t score_mode, uint8_t* k_packed, uint8_t* v_packed,
+                                   uint16_t* k_scale, uint16_t* v_scale, int32_t* kept_idx,
+                                   double* scores, void* ws, size_t ws_bytes,
+                                   wkv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * World Retrieval by camera pose ([WorldKV] Sec. 4.2 retrieval equation
  * R = Top-k(sim(a_cur, a_i)); Sec. 5.1: distance = squared L2 translation +

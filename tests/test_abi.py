@@ -161,3 +161,27 @@ def test_attention_validation(w):
     assert f(A, MIS, A, 4, 4, 2, 64, 0.0, A, None, None, 0, None) == 5
     assert f(A, A, A, 4, 4, 2, 64, 0.0, A, MIS, None, 0, None) == 5
     assert f(A, A, A, 4, 4, 2, 64, float("inf"), A, None, None, 0, None) == 2
+
+
+def test_compress_int4_validation(w):
+    f = w._compress4
+    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, A, A, None, A, 1 << 20, None]
+    names = ["k", "v", "B", "F", "T", "H", "D", "r", "mode", "kp", "vp", "ks", "vs", "ki", "sc",
+             "ws", "wsb", "s"]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    for n in ("k", "kp", "vp", "ks", "vs", "ki"):
+        assert call(**{n: None}) == 1, n
+    for n in ("k", "kp", "vs"):
+        assert call(**{n: MIS}) == 5, n
+    assert call(D=96) == 7
+    assert call(F=5) == 2
+    assert call(r=2.0) == 3
+    assert call(mode=3) == 7
+    assert call(ws=None, wsb=0) == 6
+    assert "wkv_compress_chunk_int4" in w.wkv_last_error()
