@@ -87,8 +87,8 @@ def parse():
 def measured_traffic(cfg):
     """HBM bytes per attention call (read + write, forward + split merge) from
     the committed counter summary of this workload, or None when there is
-    none or the attention source or launch planner changed since it was
-    taken."""
+    none or the attention source (kernels and launch planner) changed since
+    it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg}.json")
     if not os.path.exists(path):
