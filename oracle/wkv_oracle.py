@@ -56,6 +56,11 @@ reason in the design notes):
   [-8, 7], value = bf16_RNE(float32(q) * float32(scale)).
 * Attention: no mask, scale 1/sqrt(D) unless given, equal query and key
   head counts, log-sum-exp in natural log.
+* Query retrieval: a stored chunk is summarised by the mean of its
+  compressed key rows and the current chunk by the mean of its query rows,
+  both per (head, dim); the score is their dot product over all heads and
+  dims (one score per chunk); the k largest are retrieved, ties to the lower
+  index, returned in ascending chunk index.
 """
 
 from __future__ import annotations
@@ -320,6 +325,47 @@ def compress_chunk_int4(k_bits, v_bits, F: int, T: int, r: float, score_mode: st
     kp, ks = int4_quantize(ko)
     vp, vs = int4_quantize(vo)
     return kp, vp, ks, vs, kept_idx, scores
+
+
+# ----------------------------------------------------------------------------
+# Query-based retrieval (WorldKV Sec. 4.2: sim may be a query-based importance
+# score; WorldAttention "from video attention to long interaction" pipeline:
+# pages are scored by the dot product of the mean query and the mean key)
+# ----------------------------------------------------------------------------
+
+def mean_rows(x_bits, rows=None) -> np.ndarray:
+    """Mean over token rows, float64. x_bits: bf16 bits [B][L_in][H][D] (or
+    [L_in][H][D]); rows: optional int array [B][L] (or [L]) naming the rows
+    averaged (default: all L_in). Returns [B][H][D] (or [H][D])."""
+    X = bf16_to_f64(x_bits)
+    single = X.ndim == 3
+    if single:
+        X = X[None]
+    if rows is not None:
+        r = np.asarray(rows, dtype=np.int64)
+        r = r[None] if r.ndim == 1 else r
+        X = np.stack([X[b][r[b]] for b in range(X.shape[0])])
+    m = np.sum(X, axis=1) / X.shape[1]
+    return m[0] if single else m
+
+
+def query_scores(key_means, query_mean) -> np.ndarray:
+    """Score of every stored chunk: <mean query, mean key> over all heads and
+    dims, float64 [M]. key_means [M][H][D], query_mean [H][D]."""
+    km = np.asarray(key_means, dtype=np.float64)
+    qm = np.asarray(query_mean, dtype=np.float64)
+    return np.sum(km * qm[None], axis=(1, 2))
+
+
+def query_topk(key_means, query_mean, k: int):
+    """R = Top-k by largest score (WorldKV Sec. 4.2 retrieval equation with
+    sim = the query score). Ties go to the lower chunk index; a NaN score
+    orders after every number. Returns (idx ascending int32, scores [M])."""
+    s = query_scores(key_means, query_mean)
+    M = s.shape[0]
+    key = np.where(np.isnan(s), np.inf, -s)
+    order = np.lexsort((np.arange(M), key))
+    return np.sort(order[:min(k, M)]).astype(np.int32), s
 
 
 # ----------------------------------------------------------------------------
