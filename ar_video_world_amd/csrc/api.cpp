@@ -176,6 +176,48 @@ wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t
                          kept_idx, scores, ws, ws_bytes, stream);
 }
 
+size_t wkv_mean_rows_workspace_bytes(int32_t B, int32_t L, int32_t H, int32_t D) {
+  if (B < 1 || L < 1 || H < 1 || D < 1) return 0;
+  return (size_t)B * wkv::mean_rows_slices(L) * (size_t)H * D * sizeof(double);
+}
+
+wkv_status wkv_mean_rows(const uint16_t* x, int32_t B, int32_t L_in, const int32_t* rows,
+                         int32_t L, int32_t H, int32_t D, double* out, void* ws,
+                         size_t ws_bytes, wkv_stream_t stream) {
+  if (!x || !out || !ws) return fail(WKV_ERR_NULL, "wkv_mean_rows: x, out and ws are required");
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (B < 1 || L < 1 || L_in < 1 || (!rows && L > L_in))
+    return fail(WKV_ERR_SHAPE, "wkv_mean_rows: B=%d L_in=%d L=%d", B, L_in, L);
+  if ((int64_t)B * L_in * H * D >= ((int64_t)1 << 40) || (int64_t)B * L >= ((int64_t)1 << 31))
+    return fail(WKV_ERR_SHAPE, "wkv_mean_rows: input too large");
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (rows && !aligned16(rows)))
+    return fail(WKV_ERR_ALIGN, "wkv_mean_rows: device pointers must be 16-byte aligned");
+  const size_t need = wkv_mean_rows_workspace_bytes(B, L, H, D);
+  if (ws_bytes < need)
+    return fail(WKV_ERR_WORKSPACE, "wkv_mean_rows: workspace %zu bytes < %zu needed", ws_bytes, need);
+  hipError_t e = wkv::mean_rows_launch(x, B, L_in, rows, L, H * D, static_cast<double*>(ws), out,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_mean_rows launch");
+  return WKV_OK;
+}
+
+wkv_status wkv_query_topk(const double* key_means, int32_t M, const double* query_mean,
+                          int32_t H, int32_t D, int32_t k, int32_t* out_idx, double* scores,
+                          wkv_stream_t stream) {
+  if (!key_means || !query_mean || !out_idx || !scores)
+    return fail(WKV_ERR_NULL, "wkv_query_topk: key_means, query_mean, out_idx and scores are required");
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (M < 1 || M > 8192) return fail(WKV_ERR_SHAPE, "wkv_query_topk: M=%d (1..8192)", M);
+  if (k < 1) return fail(WKV_ERR_K, "wkv_query_topk: k=%d", k);
+  if (!aligned16(key_means) || !aligned16(query_mean) || !aligned16(out_idx) || !aligned16(scores))
+    return fail(WKV_ERR_ALIGN, "wkv_query_topk: device pointers must be 16-byte aligned");
+  const int k_eff = k < M ? k : M;
+  hipError_t e = wkv::query_topk_launch(key_means, M, query_mean, H * D, k_eff, out_idx, scores,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_query_topk launch");
+  return WKV_OK;
+}
+
 wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M, const wkv_pose* query_hist,
                          int32_t n_hist, int32_t k, int32_t* out_idx, double* out_dist,
                          wkv_pose* out_query, wkv_stream_t stream) {

@@ -33,6 +33,14 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, i
                            int32_t* kept_idx, double* scores, bool need_scores,
                            double* mean_part, double* abar, hipStream_t s);
 
+// ---- query retrieval
+int mean_rows_slices(int L);
+// part: [B][slices][H*D] float64 workspace; rows may be null (all rows).
+hipError_t mean_rows_launch(const uint16_t* x, int B, int L_in, const int32_t* rows, int L,
+                            int HD, double* part, double* out, hipStream_t s);
+hipError_t query_topk_launch(const double* key_means, int M, const double* query_mean, int HD,
+                             int k_eff, int32_t* out_idx, double* scores, hipStream_t s);
+
 // ---- pose top-k
 hipError_t pose_topk_launch(const void* poses, int M, const float* last,
                             const float* prev, int n_hist, int k_eff, int32_t* out_idx,

@@ -71,6 +71,10 @@ _compress = _sig("wkv_compress_chunk", C.c_int,
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
                    _SZ, _P])
+_mean_ws = _sig("wkv_mean_rows_workspace_bytes", _SZ, [_I32] * 4)
+_mean_rows = _sig("wkv_mean_rows", C.c_int,
+                  [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _SZ, _P])
+_query_topk = _sig("wkv_query_topk", C.c_int, [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _P])
 _pose_topk = _sig("wkv_pose_topk", C.c_int,
                   [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P, _P, _P])
 _assemble = _sig("wkv_assemble_window", C.c_int,
@@ -83,7 +87,7 @@ _attn = _sig("wkv_chunk_attention", C.c_int,
 
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
-           "wkv_pose_topk",
+           "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
 
 
@@ -222,6 +226,61 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
         outs = [t[0] for t in outs]
         scores = None if scores is None else scores[0]
     return (*outs, scores)
+
+
+def wkv_mean_rows_workspace_bytes(B: int, L: int, H: int, D: int) -> int:
+    return int(_mean_ws(B, L, H, D))
+
+
+def wkv_mean_rows(x: torch.Tensor, rows=None, out=None, ws=None, stream=None):
+    """float64 mean over token rows. x: bf16 [B, L_in, H, D] (or [L_in, H, D]);
+    rows: optional int32 [B, L] (or [L]) naming the rows averaged. Returns
+    [B, H, D] (or [H, D]) float64."""
+    _bits(x, "x")
+    squeeze = x.dim() == 3
+    if squeeze:
+        x = x.unsqueeze(0)
+        if rows is not None:
+            rows = rows.unsqueeze(0)
+    B, L_in, H, D = x.shape
+    if rows is not None:
+        if rows.dtype != torch.int32 or not rows.is_contiguous() or rows.shape[0] != B:
+            raise ValueError("rows must be a contiguous int32 [B, L] tensor")
+        L = rows.shape[1]
+    else:
+        L = L_in
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float64, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(wkv_mean_rows_workspace_bytes(B, L, H, D), 16), dtype=torch.uint8,
+                         device=x.device)
+    st = _mean_rows(_ptr(x), B, L_in, _ptr(rows), L, H, D, _ptr(out), _ptr(ws), ws.numel(),
+                    _stream(stream))
+    _check("wkv_mean_rows", st)
+    return out[0] if squeeze else out
+
+
+def wkv_query_topk(key_means: torch.Tensor, query_mean: torch.Tensor, k: int, out_idx=None,
+                   scores=None, stream=None):
+    """Top-k stored chunks by <mean query, mean key>. key_means: float64
+    [M, H, D]; query_mean: float64 [H, D]. Returns (idx int32 [min(k, M)]
+    ascending, scores float64 [M])."""
+    if key_means.dtype != torch.float64 or query_mean.dtype != torch.float64:
+        raise ValueError("key_means and query_mean must be float64")
+    if not (key_means.is_contiguous() and query_mean.is_contiguous()):
+        raise ValueError("key_means and query_mean must be contiguous")
+    M, H, D = key_means.shape
+    if tuple(query_mean.shape) != (H, D):
+        raise ValueError(f"query_mean shape {tuple(query_mean.shape)} != {(H, D)}")
+    dev = key_means.device
+    if out_idx is None:
+        out_idx = torch.empty((max(min(k, M), 1),), dtype=torch.int32, device=dev)
+    if scores is None:
+        scores = torch.empty((M,), dtype=torch.float64, device=dev)
+    st = _query_topk(_ptr(key_means), M, _ptr(query_mean), H, D, k, _ptr(out_idx), _ptr(scores),
+                     _stream(stream))
+    _check("wkv_query_topk", st)
+    return out_idx[:min(k, M)], scores
 
 
 def _pose_tuple(p) -> wkv_pose:

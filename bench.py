@@ -279,6 +279,45 @@ def main():
             comp_modes[f"{mode}/{fmt}"] = statistics.fmean(e[0].elapsed_time(e[1]) for e in cev)
         del q4
 
+        # ---- query-based retrieval, timed on its own: the mean key of the
+        # chunk just compressed (store time), the mean query of the current
+        # chunk, and the top-k over the bank's mean keys
+        qr = None
+        if not c["int4"]:
+            km_bank = w.wkv_mean_rows(bank["k"])                      # [M, H, D] float64
+            mws = torch.empty(max(w.wkv_mean_rows_workspace_bytes(1, max(Lc, Nq), H, D), 16),
+                              dtype=torch.uint8, device=dev)
+            kmo = torch.empty((1, H, D), dtype=torch.float64, device=dev)
+            qmo = torch.empty((1, H, D), dtype=torch.float64, device=dev)
+            qidx = torch.empty((k,), dtype=torch.int32, device=dev)
+            qsc = torch.empty((M,), dtype=torch.float64, device=dev)
+            qev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(20)]
+            for i in range(25):
+                s = sets[i % len(sets)]
+                e = qev[i - 5] if i >= 5 else None
+                if e:
+                    e[0].record()
+                w.wkv_mean_rows(s["ko"][None], out=kmo, ws=mws)
+                if e:
+                    e[1].record()
+                w.wkv_mean_rows(s["q"][0][None], out=qmo, ws=mws)
+                if e:
+                    e[2].record()
+                w.wkv_query_topk(km_bank, qmo[0], k, out_idx=qidx, scores=qsc)
+                if e:
+                    e[3].record()
+            torch.cuda.synchronize()
+            t_mk = statistics.fmean(e[0].elapsed_time(e[1]) for e in qev)
+            t_mq = statistics.fmean(e[1].elapsed_time(e[2]) for e in qev)
+            t_tk = statistics.fmean(e[2].elapsed_time(e[3]) for e in qev)
+            R = H * D * 2
+            qr = {"mean_key_us": round(t_mk * 1e3, 2),
+                  "mean_key_GBps": round(Lc * R / (t_mk * 1e-3) / 1e9, 1),
+                  "mean_query_us": round(t_mq * 1e3, 2),
+                  "mean_query_GBps": round(Nq * R / (t_mq * 1e-3) / 1e9, 1),
+                  "query_topk_us": round(t_tk * 1e3, 2)}
+            del km_bank, mws
+
         copy_gbps = None
         if a.copy_probe:
             src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -332,6 +371,7 @@ def main():
                                                  / (v * 1e-3) / 1e9, 1)}
                                for m, v in comp_modes.items()},
             "pose_topk_us": round(pose_ms * 1e3, 2),
+            "query_retrieval": qr,
             "assemble_us": round(asm_ms * 1e3, 2),
             "assemble_GBps": round(asm_b / (asm_ms * 1e-3) / 1e9, 1),
             "assemble_bytes": int(asm_b),

@@ -196,6 +196,45 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
                          wkv_pose* out_query, wkv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Query-based World Retrieval ([WorldKV] Sec. 4.2: sim(a_cur, a_i) may be a
+ * query-based importance score; [WorldAttention] pipeline: a page is scored
+ * by the dot product of the current mean query and the page's mean key).
+ *
+ * A stored chunk is summarised by the float64 mean of its key rows, the
+ * current chunk by the mean of its query rows (wkv_mean_rows), per (head,
+ * dim). The score of chunk m is, in float64,
+ *     s_m = sum_h sum_d key_means[m][h][d] * query_mean[h][d]
+ * and the k_eff = min(k, M) largest (s_m, lower index first; NaN orders
+ * last) are returned in ascending chunk index.
+ * ------------------------------------------------------------------------ */
+
+/* [host] Workspace bytes wkv_mean_rows needs for B units of L rows. */
+size_t wkv_mean_rows_workspace_bytes(int32_t B, int32_t L, int32_t H, int32_t D);
+
+/* out[b][h][d] = (1/L) * sum_i x[b][rows[b][i]][h][d] in float64.
+ *   x      bf16 [B][L_in][H][D]                 input rows
+ *   rows   int32 [B][L] or NULL                 rows averaged (NULL: the
+ *                                               first L = L_in rows); an id
+ *                                               outside [0, L_in) adds zeros
+ *   out    double [B][H][D]                     output
+ *   ws     >= wkv_mean_rows_workspace_bytes(B, L, H, D) bytes
+ * Limits: B >= 1; 1 <= L; L <= L_in when rows is NULL; H*D <= 8192, D in
+ * {64, 128}. Bitwise reproducible (fixed summation order). */
+wkv_status wkv_mean_rows(const uint16_t* x, int32_t B, int32_t L_in, const int32_t* rows,
+                         int32_t L, int32_t H, int32_t D, double* out, void* ws,
+                         size_t ws_bytes, wkv_stream_t stream);
+
+/* Top-k stored chunks by query score.
+ *   key_means   double [M][H][D]    mean key of each stored chunk
+ *   query_mean  double [H][D]       mean query of the current chunk
+ *   out_idx     int32 [min(k, M)]   ascending chunk index
+ *   scores      double [M]          output: every chunk's score (required)
+ * Limits: 1 <= M <= 8192; k >= 1 (k > M is clamped). */
+wkv_status wkv_query_topk(const double* key_means, int32_t M, const double* query_mean,
+                          int32_t H, int32_t D, int32_t k, int32_t* out_idx, double* scores,
+                          wkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Window assembly ([WorldKV] Sec. 4.2: retrieved KV is inserted back into the
  * native attention window without re-encoding; Sec. 5.1: the window is
  * sink | retrieval | recent | denoising; [WorldAttention] kernel section:

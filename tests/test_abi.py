@@ -185,3 +185,31 @@ def test_compress_int4_validation(w):
     assert call(mode=3) == 7
     assert call(ws=None, wsb=0) == 6
     assert "wkv_compress_chunk_int4" in w.wkv_last_error()
+
+
+def test_query_retrieval_validation(w):
+    assert w.wkv_mean_rows_workspace_bytes(2, 100, 12, 128) == 2 * 2 * 12 * 128 * 8
+    assert w.wkv_mean_rows_workspace_bytes(0, 100, 12, 128) == 0
+    f = w._mean_rows
+    ok = [A, 1, 100, None, 100, 2, 64, A, A, 1 << 20, None]
+    names = ["x", "B", "Lin", "rows", "L", "H", "D", "out", "ws", "wsb", "s"]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(x=None) == 1 and call(ws=None) == 1
+    assert call(D=32) == 7
+    assert call(L=101) == 2                 # more rows than the input holds
+    assert call(L=0) == 2
+    assert call(out=MIS) == 5
+    assert call(wsb=100) == 6
+    q = w._query_topk
+    assert q(None, 4, A, 2, 64, 1, A, A, None) == 1
+    assert q(A, 4, A, 2, 64, 1, A, None, None) == 1
+    assert q(A, 0, A, 2, 64, 1, A, A, None) == 2
+    assert q(A, 8193, A, 2, 64, 1, A, A, None) == 2
+    assert q(A, 4, A, 2, 64, 0, A, A, None) == 4
+    assert q(A, 4, MIS, 2, 64, 1, A, A, None) == 5
