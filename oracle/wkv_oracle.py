@@ -49,6 +49,9 @@ reason in the design notes):
   candidates (0 when its range is 0); the k smallest (D, index) pairs are
   returned in ascending chunk index.
 * Query-pose extrapolation: q = last + (last - prev), yaw wrapped.
+* Full-rotation poses: a unit quaternion per pose; the rotation term is the
+  SO(3) geodesic angle 2*atan2(|r_xyz|, |r_w|) of r = conj(q_i) * q_query,
+  min-max normalised like the yaw term.
 * Window order: sink | retrieved chunks in ascending chunk id | recent
   segments in temporal order | current chunk.
 * int4 store: symmetric groups of 32 along D within one (token, head) row,
@@ -251,6 +254,48 @@ def pose_topk(poses, query, k: int):
     order = np.lexsort((np.arange(M), d))
     idx = np.sort(order[:k_eff]).astype(np.int32)
     return idx, d[idx]
+
+
+def rotation_geodesic(qa, qb) -> np.ndarray:
+    """Geodesic distance on SO(3) between the rotations of quaternions qa and
+    qb ([..., 4] as w, x, y, z; any non-zero norm), float64 in [0, pi].
+
+    WorldKV Sec. 5.1: the rotation term of the retrieval distance is the
+    geodesic distance. With r = conj(qa) * qb (the relative rotation), the
+    angle is 2 * atan2(|r_xyz|, |r_w|); both parts scale with the norms, so
+    unnormalised quaternions give the same angle, and q and -q agree.
+    """
+    a = np.asarray(qa, dtype=np.float64)
+    b = np.asarray(qb, dtype=np.float64)
+    wa, va = a[..., 0], a[..., 1:]
+    wb, vb = b[..., 0], b[..., 1:]
+    w = wa * wb + np.sum(va * vb, axis=-1)
+    v = wa[..., None] * vb - wb[..., None] * va - np.cross(va, vb)
+    return 2.0 * np.arctan2(np.sqrt(np.sum(v * v, axis=-1)), np.abs(w))
+
+
+def pose_distances_so3(poses, query) -> np.ndarray:
+    """Retrieval distance with full rotations, float64 [M]. poses: float32
+    [M][8] as x, y, z, qw, qx, qy, qz, (unused); query: the same 8 (or 7)
+    floats. Squared L2 translation plus the SO(3) geodesic angle, each
+    min-max normalised over the candidates (WorldKV Sec. 5.1)."""
+    P = np.asarray(poses, dtype=np.float32).astype(np.float64)
+    q = np.asarray(query, dtype=np.float32).astype(np.float64)
+    dx = P[:, 0] - q[0]
+    dy = P[:, 1] - q[1]
+    dz = P[:, 2] - q[2]
+    dtr = (dx * dx + dy * dy) + dz * dz
+    drot = rotation_geodesic(P[:, 3:7], q[None, 3:7])
+    return _minmax(dtr) + _minmax(drot)
+
+
+def pose_topk_so3(poses, query, k: int):
+    """Top-k smallest SO(3) pose distances, ties to the lower index, returned
+    in ascending chunk index. Returns (idx int32, distances float64 [M])."""
+    d = pose_distances_so3(poses, query)
+    M = d.shape[0]
+    order = np.lexsort((np.arange(M), np.where(np.isnan(d), np.inf, d)))
+    return np.sort(order[:min(k, M)]).astype(np.int32), d
 
 
 def pose_extrapolate(prev, last) -> np.ndarray:

@@ -240,3 +240,97 @@ def test_compress_chunk_int4_is_compress_then_quantise():
         xs = O.bf16_to_f64(ref)
         s = np.repeat(O.bf16_to_f64(sb), 32, axis=-1)
         assert np.all(np.abs(xr - xs) <= 0.5 * s * (1 + 2 ** -7) + np.abs(xr) * 2 ** -8 + 1e-30)
+
+
+# ---------------------------------------------------------------- SO(3) poses
+
+def _axis_angle(axis, ang):
+    axis = np.asarray(axis, dtype=np.float64)
+    axis = axis / np.linalg.norm(axis)
+    return np.concatenate([[np.cos(ang / 2)], np.sin(ang / 2) * axis])
+
+
+def _qmul(a, b):
+    w1, v1, w2, v2 = a[0], a[1:], b[0], b[1:]
+    return np.concatenate([[w1 * w2 - v1 @ v2], w1 * v2 + w2 * v1 + np.cross(v1, v2)])
+
+
+def _rotmat(q):
+    w, x, y, z = q / np.linalg.norm(q)
+    return np.array([[1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)],
+                     [2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)],
+                     [2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)]])
+
+
+def test_geodesic_known_angles():
+    ident = np.array([1.0, 0, 0, 0])
+    assert O.rotation_geodesic(ident, _axis_angle([0, 1, 0], np.pi / 2)) == pytest.approx(np.pi / 2, abs=1e-15)
+    assert O.rotation_geodesic(ident, np.array([0.0, 1, 0, 0])) == np.pi        # 180 deg about x
+    q = _axis_angle([1, 2, 3], 0.7)
+    assert O.rotation_geodesic(q, -q) == 0.0                                   # double cover
+    assert O.rotation_geodesic(q, 2.0 * q) == 0.0                              # scale free
+    assert O.rotation_geodesic(q, q) == 0.0
+
+
+def test_geodesic_matches_rotation_matrix_trace():
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        a = rng.standard_normal(4)
+        ang = rng.uniform(0.2, 2.9)
+        b = _qmul(a / np.linalg.norm(a), _axis_angle(rng.standard_normal(3), ang))
+        Ra, Rb = _rotmat(a), _rotmat(b)
+        ref = np.arccos((np.trace(Ra.T @ Rb) - 1) / 2)
+        assert abs(O.rotation_geodesic(a, b) - ref) < 1e-12
+        assert abs(ref - ang) < 1e-12
+        g = rng.standard_normal(4)                                             # bi-invariance
+        assert abs(O.rotation_geodesic(_qmul(g, a), _qmul(g, b)) - ref) < 1e-12
+        assert O.rotation_geodesic(a, b) == O.rotation_geodesic(b, a)
+
+
+def test_so3_distances_reduce_to_yaw_for_z_rotations():
+    rng = np.random.default_rng(8)
+    M = 30
+    yaw = rng.uniform(-np.pi, np.pi, M + 1).astype(np.float32)
+    t = rng.standard_normal((M + 1, 3)).astype(np.float32)
+    # yaw differences are taken between float32 angles: build the quaternions
+    # in float64 from those angles and compare against the yaw form
+    P = np.zeros((M + 1, 8))
+    P[:, :3] = t
+    P[:, 3] = np.cos(yaw.astype(np.float64) / 2)
+    P[:, 6] = np.sin(yaw.astype(np.float64) / 2)
+    drot_so3 = O.rotation_geodesic(P[:M, 3:7], P[M, 3:7][None])
+    drot_yaw = np.abs(O.wrap_angle(yaw[:M].astype(np.float64) - float(yaw[M])))
+    assert np.max(np.abs(drot_so3 - drot_yaw)) < 1e-12
+
+
+def test_so3_topk_against_full_sort():
+    rng = np.random.default_rng(9)
+    M = 50
+    P = np.zeros((M, 8), dtype=np.float32)
+    P[:, :3] = rng.standard_normal((M, 3))
+    P[:, 3:7] = rng.standard_normal((M, 4))
+    P[17] = P[4]                                                               # exact tie
+    q = P[4].copy()
+    d = O.pose_distances_so3(P, q)
+    assert d[4] == 0.0 and d[17] == 0.0
+    for k in (1, 2, 5, 50, 60):
+        idx, _ = O.pose_topk_so3(P, q, k)
+        ref = sorted(sorted(range(M), key=lambda i: (d[i], i))[:k])
+        assert list(idx) == ref
+
+
+def test_so3_worked_example_by_hand():
+    # query at the origin, identity rotation
+    # pose 0: t=(1,0,0), identity          -> dtr 1, angle 0
+    # pose 1: t=(0,0,0), 180 deg about x   -> dtr 0, angle pi
+    # pose 2: t=(2,0,0), 90 deg about z    -> dtr 4, angle pi/2
+    # min-max: dtr -> 1/4, 0, 1; angle -> 0, 1, 1/2; D = 1/4, 1, 3/2
+    P = np.zeros((3, 8), dtype=np.float32)
+    P[0, :4] = (1, 0, 0, 1)
+    P[1, 3:7] = (0, 1, 0, 0)
+    P[2, :3] = (2, 0, 0)
+    P[2, 3:7] = (np.cos(np.pi / 4), 0, 0, np.sin(np.pi / 4))
+    q = np.array([0, 0, 0, 1, 0, 0, 0, 0], dtype=np.float32)
+    d = O.pose_distances_so3(P, q)
+    assert d[0] == 0.25 and d[1] == 1.0 and abs(d[2] - 1.5) < 1e-7
+    assert list(O.pose_topk_so3(P, q, 2)[0]) == [0, 1]
