@@ -13,6 +13,9 @@
 
 #include "wkv_internal.hpp"
 
+static_assert(sizeof(wkv_pose) == 16, "wkv_pose is read as one float4 per pose");
+static_assert(sizeof(wkv_pose_q) == 32, "wkv_pose_q is read as two float4 per pose");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -235,6 +238,22 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M, const wkv_pose* 
   hipError_t e = wkv::pose_topk_launch(bank_poses, M, last, prev, n_hist, k_eff, out_idx,
                                        out_dist, out_query, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "wkv_pose_topk launch");
+  return WKV_OK;
+}
+
+wkv_status wkv_pose_topk_so3(const wkv_pose_q* bank_poses, int32_t M, const wkv_pose_q* query,
+                             int32_t k, int32_t* out_idx, double* out_dist,
+                             wkv_stream_t stream) {
+  if (!bank_poses || !query || !out_idx)
+    return fail(WKV_ERR_NULL, "wkv_pose_topk_so3: bank_poses, query and out_idx are required");
+  if (M < 1 || M > 8192) return fail(WKV_ERR_SHAPE, "wkv_pose_topk_so3: M=%d not in [1, 8192]", M);
+  if (k < 1) return fail(WKV_ERR_K, "wkv_pose_topk_so3: k=%d < 1", k);
+  if (!aligned16(bank_poses) || !aligned16(out_idx) || (out_dist && !aligned16(out_dist)))
+    return fail(WKV_ERR_ALIGN, "wkv_pose_topk_so3: device pointers must be 16-byte aligned");
+  const int k_eff = k < M ? k : M;
+  hipError_t e = wkv::pose_topk_so3_launch(bank_poses, M, &query->x, k_eff, out_idx, out_dist,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_pose_topk_so3 launch");
   return WKV_OK;
 }
 

@@ -46,6 +46,10 @@ hipError_t pose_topk_launch(const void* poses, int M, const float* last,
                             const float* prev, int n_hist, int k_eff, int32_t* out_idx,
                             double* out_dist, void* out_query, hipStream_t s);
 
+// poses: 32-byte records (x, y, z, qw, qx, qy, qz, pad); query: 7 floats.
+hipError_t pose_topk_so3_launch(const void* poses, int M, const float* query, int k_eff,
+                                int32_t* out_idx, double* out_dist, hipStream_t s);
+
 // ---- window assembly
 struct AssemblePlan {
   const uint16_t* seg_k[kMaxSegments];

@@ -42,6 +42,11 @@ class wkv_pose(C.Structure):
     _fields_ = [("x", C.c_float), ("y", C.c_float), ("z", C.c_float), ("yaw", C.c_float)]
 
 
+class wkv_pose_q(C.Structure):
+    _fields_ = [("x", C.c_float), ("y", C.c_float), ("z", C.c_float), ("qw", C.c_float),
+                ("qx", C.c_float), ("qy", C.c_float), ("qz", C.c_float), ("pad", C.c_float)]
+
+
 class wkv_segment(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n", C.c_int32)]
 
@@ -71,6 +76,8 @@ _compress = _sig("wkv_compress_chunk", C.c_int,
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
                    _SZ, _P])
+_pose_so3 = _sig("wkv_pose_topk_so3", C.c_int,
+                 [_P, _I32, C.POINTER(wkv_pose_q), _I32, _P, _P, _P])
 _mean_ws = _sig("wkv_mean_rows_workspace_bytes", _SZ, [_I32] * 4)
 _mean_rows = _sig("wkv_mean_rows", C.c_int,
                   [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _SZ, _P])
@@ -88,6 +95,7 @@ _attn = _sig("wkv_chunk_attention", C.c_int,
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
+           "wkv_pose_topk_so3",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
 
 
@@ -226,6 +234,28 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
         outs = [t[0] for t in outs]
         scores = None if scores is None else scores[0]
     return (*outs, scores)
+
+
+def wkv_pose_topk_so3(poses: torch.Tensor, query, k: int, want_dist: bool = True,
+                      out_idx=None, out_dist=None, stream=None):
+    """Pose top-k with full rotations. poses: float32 [M, 8] device tensor
+    (x, y, z, qw, qx, qy, qz, pad); query: 7 or 8 floats. Returns
+    (idx int32 [k_eff], dist float64 [k_eff] or None)."""
+    if poses.dtype != torch.float32 or poses.dim() != 2 or poses.shape[1] != 8 or \
+            not poses.is_contiguous():
+        raise ValueError("poses must be a contiguous float32 [M, 8] tensor")
+    M = poses.shape[0]
+    k_eff = min(k, M)
+    q = [float(t) for t in query][:7] + [0.0]
+    qs = wkv_pose_q(*q)
+    dev = poses.device
+    if out_idx is None:
+        out_idx = torch.empty((max(k_eff, 1),), dtype=torch.int32, device=dev)
+    if want_dist and out_dist is None:
+        out_dist = torch.empty((max(k_eff, 1),), dtype=torch.float64, device=dev)
+    st = _pose_so3(_ptr(poses), M, C.byref(qs), k, _ptr(out_idx), _ptr(out_dist), _stream(stream))
+    _check("wkv_pose_topk_so3", st)
+    return out_idx[:k_eff], (out_dist[:k_eff] if out_dist is not None else None)
 
 
 def wkv_mean_rows_workspace_bytes(B: int, L: int, H: int, D: int) -> int:

@@ -318,6 +318,25 @@ def main():
                   "query_topk_us": round(t_tk * 1e3, 2)}
             del km_bank, mws
 
+        # ---- pose top-k with full rotations (the walk's yaw as z-axis
+        # quaternions), timed on its own
+        P8 = torch.zeros((M, 8), dtype=torch.float32, device=dev)
+        P8[:, :3] = poses[:, :3]
+        P8[:, 3] = torch.cos(poses[:, 3].double() / 2).float()
+        P8[:, 6] = torch.sin(poses[:, 3].double() / 2).float()
+        qq = qhist[-1]
+        q8 = [qq[0], qq[1], qq[2], math.cos(qq[3] / 2), 0.0, 0.0, math.sin(qq[3] / 2)]
+        sidx = torch.empty((k,), dtype=torch.int32, device=dev)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        for i in range(25):
+            if i >= 5:
+                pev[i - 5][0].record()
+            w.wkv_pose_topk_so3(P8, q8, k, want_dist=False, out_idx=sidx)
+            if i >= 5:
+                pev[i - 5][1].record()
+        torch.cuda.synchronize()
+        t_so3 = statistics.fmean(e[0].elapsed_time(e[1]) for e in pev)
+
         copy_gbps = None
         if a.copy_probe:
             src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -371,6 +390,7 @@ def main():
                                                  / (v * 1e-3) / 1e9, 1)}
                                for m, v in comp_modes.items()},
             "pose_topk_us": round(pose_ms * 1e3, 2),
+            "pose_topk_so3_us": round(t_so3 * 1e3, 2),
             "query_retrieval": qr,
             "assemble_us": round(asm_ms * 1e3, 2),
             "assemble_GBps": round(asm_b / (asm_ms * 1e-3) / 1e9, 1),

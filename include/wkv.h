@@ -60,6 +60,15 @@ typedef struct {
   float x, y, z, yaw;
 } wkv_pose;
 
+/* Camera pose with a full rotation: translation and a quaternion (w, x, y,
+ * z) of any non-zero norm ([WorldKV] Sec. 5.1 "geodesic distance in
+ * rotation"). 32 bytes; pad is ignored. */
+typedef struct {
+  float x, y, z;
+  float qw, qx, qy, qz;
+  float pad;
+} wkv_pose_q;
+
 /* A run of window rows: k, v bf16 [n][H][D] (device). n may be 0 (then k, v
  * may be NULL). */
 typedef struct {
@@ -194,6 +203,17 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
                          const wkv_pose* query_hist, int32_t n_hist, int32_t k,
                          int32_t* out_idx, double* out_dist,
                          wkv_pose* out_query, wkv_stream_t stream);
+
+/* Pose top-k with full rotations: as wkv_pose_topk with the rotation term
+ *   dr_i = 2 * atan2(|r_xyz|, |r_w|),  r = conj(q_i) * q_query
+ * (the SO(3) geodesic angle, float64 from the float32 values), min-max
+ * normalised with the translation term. The query is given (no history).
+ *   bank_poses  wkv_pose_q [M]   device, 1 <= M <= 8192
+ *   query       wkv_pose_q [1]   [host]
+ *   out_idx     int32 [min(k, M)], out_dist double [min(k, M)] (NULL ok) */
+wkv_status wkv_pose_topk_so3(const wkv_pose_q* bank_poses, int32_t M, const wkv_pose_q* query,
+                             int32_t k, int32_t* out_idx, double* out_dist,
+                             wkv_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Query-based World Retrieval ([WorldKV] Sec. 4.2: sim(a_cur, a_i) may be a

@@ -213,3 +213,16 @@ def test_query_retrieval_validation(w):
     assert q(A, 8193, A, 2, 64, 1, A, A, None) == 2
     assert q(A, 4, A, 2, 64, 0, A, A, None) == 4
     assert q(A, 4, MIS, 2, 64, 1, A, A, None) == 5
+
+
+def test_pose_so3_validation(w):
+    f = w._pose_so3
+    q = w.wkv_pose_q(0, 0, 0, 1, 0, 0, 0, 0)
+    assert f(None, 4, q, 2, A, None, None) == 1
+    assert f(A, 4, None, 2, A, None, None) == 1
+    assert f(A, 4, q, 2, None, None, None) == 1
+    assert f(A, 0, q, 2, A, None, None) == 2
+    assert f(A, 8193, q, 2, A, None, None) == 2
+    assert f(A, 4, q, 0, A, None, None) == 4
+    assert f(MIS, 4, q, 2, A, None, None) == 5
+    assert C.sizeof(w.wkv_pose_q) == 32
