@@ -49,6 +49,9 @@ reason in the design notes):
   candidates (0 when its range is 0); the k smallest (D, index) pairs are
   returned in ascending chunk index.
 * Query-pose extrapolation: q = last + (last - prev), yaw wrapped.
+* Host tier: staging slots in HBM filled least recently used first (ties to
+  the lower slot); a retrieved chunk that is not staged is replaced by the
+  staged predicted chunk of the same rank.
 * Full-rotation poses: a unit quaternion per pose; the rotation term is the
   SO(3) geodesic angle 2*atan2(|r_xyz|, |r_w|) of r = conj(q_i) * q_query,
   min-max normalised like the yaw term.
@@ -411,6 +414,64 @@ def query_topk(key_means, query_mean, k: int):
     key = np.where(np.isnan(s), np.inf, -s)
     order = np.lexsort((np.arange(M), key))
     return np.sort(order[:min(k, M)]).astype(np.int32), s
+
+
+# ----------------------------------------------------------------------------
+# Host tier (WorldKV Sec. 4.2: evicted chunks are kept in GPU/CPU memory;
+# WorldPager abstract and Fig. 2: the int4 store lives in pinned host memory,
+# the next chunk's retrieval set is prefetched from the extrapolated pose, and
+# a miss reuses what is staged instead of stalling)
+# ----------------------------------------------------------------------------
+
+def tier_plan(slot_chunk, last_use, clock: int, ids):
+    """Stage the chunks `ids` (distinct) into HBM slots, least recently used
+    first. slot_chunk / last_use: lists over the slots (chunk -1 = empty,
+    stamp 0 = never used); clock: the last stamp handed out.
+
+    The request gets stamp clock + 1. An id already held keeps its slot. Each
+    other id, in request order, takes the slot with the smallest (stamp, slot
+    index) among the slots that hold no id of this request, and is copied.
+    Returns (slot_chunk, last_use, clock, slot_of, copies) with copies a list
+    of (id, slot)."""
+    sc = list(slot_chunk)
+    lu = list(last_use)
+    clock += 1
+    slot_of = [-1] * len(ids)
+    taken = [False] * len(sc)
+    for i, c in enumerate(ids):
+        for s_, held in enumerate(sc):
+            if held == c:
+                slot_of[i] = s_
+                taken[s_] = True
+                lu[s_] = clock
+                break
+    copies = []
+    for i, c in enumerate(ids):
+        if slot_of[i] >= 0:
+            continue
+        cand = [(lu[s_], s_) for s_ in range(len(sc)) if not taken[s_]]
+        _, v = min(cand)
+        sc[v] = c
+        lu[v] = clock
+        taken[v] = True
+        slot_of[i] = v
+        copies.append((c, v))
+    return sc, lu, clock, slot_of, copies
+
+
+def tier_resolve(actual, slot_chunk, pred_slot):
+    """Staging slot of every retrieved chunk: the slot holding it, or on a
+    miss the slot of the predicted chunk of the same rank (the staged,
+    possibly stale, chunk is used instead of waiting). Returns (slots,
+    number of misses)."""
+    out, miss = [], 0
+    for j, a in enumerate(actual):
+        s_ = next((i for i, c in enumerate(slot_chunk) if a >= 0 and c == a), -1)
+        if s_ < 0:
+            s_ = pred_slot[j]
+            miss += 1
+        out.append(s_)
+    return out, miss
 
 
 # ----------------------------------------------------------------------------
