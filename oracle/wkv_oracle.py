@@ -50,8 +50,8 @@ reason in the design notes):
   returned in ascending chunk index.
 * Query-pose extrapolation: q = last + (last - prev), yaw wrapped.
 * Host tier: staging slots in HBM filled least recently used first (ties to
-  the lower slot); a retrieved chunk that is not staged is replaced by the
-  staged predicted chunk of the same rank.
+  the lower slot); retrieved chunks that are not staged are replaced, in
+  rank order, by the staged predicted chunks no hit uses.
 * Full-rotation poses: a unit quaternion per pose; the rotation term is the
   SO(3) geodesic angle 2*atan2(|r_xyz|, |r_w|) of r = conj(q_i) * q_query,
   min-max normalised like the yaw term.
@@ -460,17 +460,22 @@ def tier_plan(slot_chunk, last_use, clock: int, ids):
 
 
 def tier_resolve(actual, slot_chunk, pred_slot):
-    """Staging slot of every retrieved chunk: the slot holding it, or on a
-    miss the slot of the predicted chunk of the same rank (the staged,
-    possibly stale, chunk is used instead of waiting). Returns (slots,
-    number of misses)."""
+    """Staging slot of every retrieved chunk: the slot holding it (a hit), or
+    on a miss a staged predicted chunk instead of waiting for a copy. The
+    misses, in rank order, take the predicted slots (in rank order) that no
+    hit uses, so no chunk appears twice. A negative id is a miss. Returns
+    (slots, number of misses)."""
+    hit = []
+    for a in actual:
+        hit.append(next((i for i, c in enumerate(slot_chunk) if a >= 0 and c == a), -1))
+    spare = [p_ for p_ in pred_slot[:len(actual)] if p_ not in hit]
     out, miss = [], 0
-    for j, a in enumerate(actual):
-        s_ = next((i for i, c in enumerate(slot_chunk) if a >= 0 and c == a), -1)
-        if s_ < 0:
-            s_ = pred_slot[j]
+    for h in hit:
+        if h >= 0:
+            out.append(h)
+        else:
+            out.append(spare[miss])
             miss += 1
-        out.append(s_)
     return out, miss
 
 

@@ -28,10 +28,30 @@ def test_lru_sequence_by_hand():
 
 def test_resolve_by_hand():
     slot_chunk = [9, 1, 3, 7]
+    # 8 is not staged; the predicted slots are 2, 0, 3 and hits use 1 and 3:
+    # the spare predicted slots in rank order are 2, 0 -> 8 takes slot 2
     slots, miss = O.tier_resolve([1, 7, 8], slot_chunk, [2, 0, 3])
-    assert slots == [1, 3, 3] and miss == 1          # 8 is not staged: rank 2 -> slot 3
+    assert slots == [1, 3, 2] and miss == 1
     slots, miss = O.tier_resolve([4, -1], slot_chunk, [0, 1])
     assert slots == [0, 1] and miss == 2
+    # ranks shift between prediction and retrieval: predicted 9, 3, 7 in
+    # slots 0, 2, 3; retrieved 5, 9, 3 -> hits 9 (0) and 3 (2), 5 takes 3
+    slots, miss = O.tier_resolve([5, 9, 3], slot_chunk, [0, 2, 3])
+    assert slots == [3, 0, 2] and miss == 1
+
+
+def test_resolve_never_repeats_a_slot():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        S_ = int(rng.integers(2, 20))
+        sc = [int(x) for x in rng.choice(40, size=S_, replace=False)]
+        n = int(rng.integers(1, S_ + 1))
+        pred = [int(x) for x in rng.choice(S_, size=n, replace=False)]
+        actual = [int(x) for x in rng.choice(45, size=n, replace=False)]
+        slots, miss = O.tier_resolve(actual, sc, pred)
+        assert len(set(slots)) == n
+        assert miss == sum(1 for a in actual if a not in sc)
+        assert all(sc[s_] == a for s_, a in zip(slots, actual) if a in sc)
 
 
 @pytest.mark.parametrize("seed", range(5))
