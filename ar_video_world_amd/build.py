@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwkv.so")
 
-SOURCES = ["api.cpp", "compress.hip", "pose.hip", "retrieve.hip", "assemble.hip", "attention.hip"]
+SOURCES = ["api.cpp", "compress.hip", "pose.hip", "retrieve.hip", "tier.hip",
+           "assemble.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -5,11 +5,14 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "wkv_internal.hpp"
 
@@ -257,6 +260,146 @@ wkv_status wkv_pose_topk_so3(const wkv_pose_q* bank_poses, int32_t M, const wkv_
   return WKV_OK;
 }
 
+wkv_status wkv_tier_init(wkv_tier* t, int32_t n_slots) {
+  if (!t) return fail(WKV_ERR_NULL, "wkv_tier_init: t is NULL");
+  if (n_slots < 1 || n_slots > WKV_TIER_MAX_SLOTS)
+    return fail(WKV_ERR_SHAPE, "wkv_tier_init: n_slots=%d (1..%d)", n_slots, WKV_TIER_MAX_SLOTS);
+  std::memset(t, 0, sizeof(*t));
+  t->n_slots = n_slots;
+  for (int i = 0; i < WKV_TIER_MAX_SLOTS; ++i) t->chunk[i] = -1;
+  return WKV_OK;
+}
+
+wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* slot_of,
+                         int32_t* copy_ids, int32_t* copy_slots, int32_t* n_copies) {
+  if (!t || !ids || !slot_of || !copy_ids || !copy_slots || !n_copies)
+    return fail(WKV_ERR_NULL, "wkv_tier_plan: null argument");
+  if (t->n_slots < 1 || t->n_slots > WKV_TIER_MAX_SLOTS)
+    return fail(WKV_ERR_SHAPE, "wkv_tier_plan: table not initialised (n_slots=%d)", t->n_slots);
+  if (n < 1 || n > t->n_slots)
+    return fail(WKV_ERR_SHAPE, "wkv_tier_plan: n=%d (1..n_slots=%d)", n, t->n_slots);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0) return fail(WKV_ERR_SHAPE, "wkv_tier_plan: ids[%d]=%d < 0", i, ids[i]);
+    for (int j = 0; j < i; ++j)
+      if (ids[j] == ids[i]) return fail(WKV_ERR_SHAPE, "wkv_tier_plan: id %d repeated", ids[i]);
+  }
+  const uint64_t stamp = ++t->clock;
+  bool taken[WKV_TIER_MAX_SLOTS] = {};
+  for (int i = 0; i < n; ++i) {
+    slot_of[i] = -1;
+    for (int s = 0; s < t->n_slots; ++s)
+      if (t->chunk[s] == ids[i]) {
+        slot_of[i] = s;
+        taken[s] = true;
+        t->last_use[s] = stamp;
+        break;
+      }
+  }
+  int nc = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slot_of[i] >= 0) continue;
+    int v = -1;
+    for (int s = 0; s < t->n_slots; ++s)
+      if (!taken[s] && (v < 0 || t->last_use[s] < t->last_use[v])) v = s;  // ties: lower slot
+    t->chunk[v] = ids[i];
+    t->last_use[v] = stamp;
+    taken[v] = true;
+    slot_of[i] = v;
+    copy_ids[nc] = ids[i];
+    copy_slots[nc] = v;
+    ++nc;
+  }
+  *n_copies = nc;
+  return WKV_OK;
+}
+
+wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n,
+                             const wkv_bank* host_bank, const wkv_bank* staging, int32_t H,
+                             int32_t D, int32_t* dev_slot_chunk, int32_t* dev_pred_slot,
+                             int32_t* n_copies, wkv_stream_t stream) {
+  if (!t || !ids || !host_bank || !staging || !dev_slot_chunk || !dev_pred_slot || !n_copies)
+    return fail(WKV_ERR_NULL, "wkv_tier_prefetch: null argument");
+  if (wkv_status st = check_hd(H, D)) return st;
+  const bool q4 = host_bank->dtype == WKV_BANK_INT4_G32;
+  if ((host_bank->dtype != WKV_BANK_BF16 && !q4) || staging->dtype != host_bank->dtype ||
+      staging->Lc != host_bank->Lc || host_bank->Lc < 1 || host_bank->M < 1 ||
+      staging->M != t->n_slots)
+    return fail(WKV_ERR_SHAPE, "wkv_tier_prefetch: host bank and staging bank do not match the table");
+  if (!host_bank->k || !host_bank->v || !staging->k || !staging->v ||
+      (q4 && (!host_bank->k_scale || !host_bank->v_scale || !staging->k_scale || !staging->v_scale)))
+    return fail(WKV_ERR_NULL, "wkv_tier_prefetch: bank pointers are required");
+  for (int i = 0; i < n; ++i)
+    if (ids[i] >= host_bank->M)
+      return fail(WKV_ERR_SHAPE, "wkv_tier_prefetch: ids[%d]=%d >= M=%d", i, ids[i], host_bank->M);
+  if (!aligned16(dev_slot_chunk) || !aligned16(dev_pred_slot))
+    return fail(WKV_ERR_ALIGN, "wkv_tier_prefetch: device pointers must be 16-byte aligned");
+  // Plan on a copy of the table: nothing changes unless every enqueue succeeds.
+  wkv_tier nt = *t;
+  int32_t slot_of[WKV_TIER_MAX_SLOTS], cid[WKV_TIER_MAX_SLOTS], cslot[WKV_TIER_MAX_SLOTS], nc = 0;
+  if (wkv_status st = wkv_tier_plan(&nt, ids, n, slot_of, cid, cslot, &nc)) return st;
+  const size_t rows = (size_t)host_bank->Lc * H * D;
+  const size_t kv_bytes = q4 ? rows / 2 : rows * 2;
+  const size_t sc_bytes = q4 ? rows / 32 * 2 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nc > 0) {
+    // The copies read the host bank through its device mapping (pinned
+    // memory allocated with hipHostMalloc is mapped); anything else is
+    // refused here rather than touched by the kernel.
+    const void* hsrc[4] = {host_bank->k, host_bank->v, host_bank->k_scale, host_bank->v_scale};
+    void* ddst[4] = {const_cast<void*>(staging->k), const_cast<void*>(staging->v),
+                     const_cast<uint16_t*>(staging->k_scale), const_cast<uint16_t*>(staging->v_scale)};
+    wkv::TierCopy c;
+    std::memset(&c, 0, sizeof(c));
+    c.narr = q4 ? 4 : 2;
+    c.n = nc;
+    for (int a = 0; a < c.narr; ++a) {
+      void* dp = nullptr;
+      hipError_t e = hipHostGetDevicePointer(&dp, const_cast<void*>(hsrc[a]), 0);
+      if (e != hipSuccess || !dp)
+        return fail(WKV_ERR_UNSUPPORTED,
+                    "wkv_tier_prefetch: the host bank must be pinned, device-mapped host memory (%s)",
+                    hipGetErrorString(e));
+      c.src[a] = static_cast<const uint8_t*>(dp);
+      c.dst[a] = static_cast<uint8_t*>(ddst[a]);
+      c.bytes[a] = a < 2 ? kv_bytes : sc_bytes;
+    }
+    for (int i = 0; i < nc; ++i) {
+      c.id[i] = cid[i];
+      c.slot[i] = cslot[i];
+    }
+    hipError_t e = wkv::tier_copy_launch(c, s);
+    if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch copy");
+  }
+  wkv::TierTable tt;
+  std::memset(&tt, 0, sizeof(tt));
+  tt.n_slots = nt.n_slots;
+  tt.n_pred = n;
+  for (int i = 0; i < nt.n_slots; ++i) tt.chunk[i] = nt.chunk[i];
+  for (int i = 0; i < n; ++i) tt.pred[i] = slot_of[i];
+  hipError_t e = wkv::tier_table_launch(tt, dev_slot_chunk, dev_pred_slot, s);
+  if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch table");
+  *t = nt;
+  *n_copies = nc;
+  return WKV_OK;
+}
+
+wkv_status wkv_tier_resolve(const int32_t* actual_idx, int32_t n, const int32_t* slot_chunk,
+                            int32_t n_slots, const int32_t* pred_slot, int32_t* out_slot,
+                            int32_t* out_miss, wkv_stream_t stream) {
+  if (!actual_idx || !slot_chunk || !pred_slot || !out_slot)
+    return fail(WKV_ERR_NULL, "wkv_tier_resolve: null argument");
+  if (n < 1 || n > WKV_TIER_MAX_SLOTS || n_slots < 1 || n_slots > WKV_TIER_MAX_SLOTS)
+    return fail(WKV_ERR_SHAPE, "wkv_tier_resolve: n=%d n_slots=%d (1..%d)", n, n_slots,
+                WKV_TIER_MAX_SLOTS);
+  if (!aligned16(actual_idx) || !aligned16(slot_chunk) || !aligned16(pred_slot) ||
+      !aligned16(out_slot) || (out_miss && !aligned16(out_miss)))
+    return fail(WKV_ERR_ALIGN, "wkv_tier_resolve: device pointers must be 16-byte aligned");
+  hipError_t e = wkv::tier_resolve_launch(actual_idx, n, slot_chunk, n_slots, pred_slot, out_slot,
+                                          out_miss, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_tier_resolve launch");
+  return WKV_OK;
+}
+
 wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,
                                const int32_t* retrieved_idx, int32_t n_ret,
                                const wkv_segment* recent, int32_t n_recent,
@@ -379,6 +522,92 @@ wkv_status wkv_chunk_attention(const uint16_t* q, const uint16_t* k, const uint1
   hipError_t e = wkv::attention_launch(q, k, v, Nq, Nk, H, D, sc, out, lse, plan, ws,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "wkv_chunk_attention launch");
+  return WKV_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Host-side retrieval planning for the host tier (WorldPager Fig. 2: the
+// camera pose is an input known before the chunk is computed, so the
+// retrieval set of the next chunk is chosen from the extrapolated pose while
+// the GPU still works on the current one, and its copies are queued ahead).
+// wkv_pose_topk_host is the pose top-k of wkv_pose_topk evaluated on the host
+// for that planning: the same float64 operation sequence (contraction off
+// from here to the end of the file), min-max normalisation, and (distance,
+// index) order with NaN last. The retrieval feeding the window stays on the
+// GPU.
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kPi = 3.1415926535897932384626433832795;
+
+double wrap_angle(double a) {
+  double w = a - kTwoPi * std::rint(a / kTwoPi);
+  if (w <= -kPi) w = w + kTwoPi;
+  if (w > kPi) w = w - kTwoPi;
+  return w;
+}
+
+double minmax(double v, double lo, double hi) { return hi == lo ? 0.0 : (v - lo) / (hi - lo); }
+
+}  // namespace
+
+
+extern "C" {
+
+wkv_status wkv_pose_topk_host(const wkv_pose* bank_poses, int32_t M, const wkv_pose* query_hist,
+                              int32_t n_hist, int32_t k, int32_t* out_idx, double* out_dist) {
+  if (!bank_poses || !query_hist || !out_idx)
+    return fail(WKV_ERR_NULL, "wkv_pose_topk_host: bank_poses, query_hist and out_idx are required");
+  if (M < 1 || M > 8192) return fail(WKV_ERR_SHAPE, "wkv_pose_topk_host: M=%d not in [1, 8192]", M);
+  if (k < 1) return fail(WKV_ERR_K, "wkv_pose_topk_host: k=%d < 1", k);
+  if (n_hist != 1 && n_hist != 2)
+    return fail(WKV_ERR_K, "wkv_pose_topk_host: n_hist=%d (must be 1 or 2)", n_hist);
+  const wkv_pose& last = query_hist[n_hist - 1];
+  double qx = last.x, qy = last.y, qz = last.z, qyaw = last.yaw;
+  if (n_hist == 2) {
+    const wkv_pose& prev = query_hist[0];
+    const double lx = last.x, ly = last.y, lz = last.z, lyaw = last.yaw;
+    qx = 2.0 * lx - (double)prev.x;
+    qy = 2.0 * ly - (double)prev.y;
+    qz = 2.0 * lz - (double)prev.z;
+    qyaw = wrap_angle(lyaw + wrap_angle(lyaw - (double)prev.yaw));
+  }
+  // the query is a float32 pose
+  const double fx = (float)qx, fy = (float)qy, fz = (float)qz, fyaw = (float)qyaw;
+  std::vector<double> dtr(M), drot(M);
+  double tmin = INFINITY, tmax = -INFINITY, rmin = INFINITY, rmax = -INFINITY;
+  for (int i = 0; i < M; ++i) {
+    const double dx = (double)bank_poses[i].x - fx;
+    const double dy = (double)bank_poses[i].y - fy;
+    const double dz = (double)bank_poses[i].z - fz;
+    dtr[i] = (dx * dx + dy * dy) + dz * dz;
+    drot[i] = std::fabs(wrap_angle((double)bank_poses[i].yaw - fyaw));
+    tmin = std::fmin(tmin, dtr[i]);
+    tmax = std::fmax(tmax, dtr[i]);
+    rmin = std::fmin(rmin, drot[i]);
+    rmax = std::fmax(rmax, drot[i]);
+  }
+  std::vector<std::pair<double, int>> key(M);
+  for (int i = 0; i < M; ++i) {
+    const double d = minmax(dtr[i], tmin, tmax) + minmax(drot[i], rmin, rmax);
+    key[i] = {std::isnan(d) ? INFINITY : d, i};
+  }
+  const int k_eff = k < M ? k : M;
+  std::partial_sort(key.begin(), key.begin() + k_eff, key.end());
+  std::vector<int> sel(k_eff);
+  for (int i = 0; i < k_eff; ++i) sel[i] = key[i].second;
+  std::sort(sel.begin(), sel.end());
+  for (int i = 0; i < k_eff; ++i) {
+    out_idx[i] = sel[i];
+    if (out_dist) {
+      const int j = sel[i];
+      out_dist[i] = minmax(dtr[j], tmin, tmax) + minmax(drot[j], rmin, rmax);
+    }
+  }
   return WKV_OK;
 }
 

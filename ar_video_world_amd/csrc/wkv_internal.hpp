@@ -50,6 +50,33 @@ hipError_t pose_topk_launch(const void* poses, int M, const float* last,
 hipError_t pose_topk_so3_launch(const void* poses, int M, const float* query, int k_eff,
                                 int32_t* out_idx, double* out_dist, hipStream_t s);
 
+// ---- host tier (device side)
+constexpr int kTierMaxSlots = 64;
+struct TierTable {
+  int32_t chunk[kTierMaxSlots];
+  int32_t pred[kTierMaxSlots];
+  int32_t n_slots;
+  int32_t n_pred;
+};
+hipError_t tier_table_launch(const TierTable& t, int32_t* slot_chunk, int32_t* pred_slot,
+                             hipStream_t s);
+// Copies of whole chunks: array a (K, V and, for int4, their scales) moves
+// bytes[a] from src[a] + id[j]*bytes[a] (device mapping of pinned host
+// memory) to dst[a] + slot[j]*bytes[a]; every bytes[a] is a multiple of 4.
+struct TierCopy {
+  const uint8_t* src[4];
+  uint8_t* dst[4];
+  size_t bytes[4];
+  int32_t id[kTierMaxSlots];
+  int32_t slot[kTierMaxSlots];
+  int32_t narr;
+  int32_t n;
+};
+hipError_t tier_copy_launch(const TierCopy& c, hipStream_t s);
+hipError_t tier_resolve_launch(const int32_t* actual, int n, const int32_t* slot_chunk,
+                               int n_slots, const int32_t* pred_slot, int32_t* out_slot,
+                               int32_t* out_miss, hipStream_t s);
+
 // ---- window assembly
 struct AssemblePlan {
   const uint16_t* seg_k[kMaxSegments];

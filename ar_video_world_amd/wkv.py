@@ -57,6 +57,14 @@ class wkv_bank(C.Structure):
                 ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
 
 
+WKV_TIER_MAX_SLOTS = 64
+
+
+class wkv_tier(C.Structure):
+    _fields_ = [("n_slots", C.c_int32), ("chunk", C.c_int32 * WKV_TIER_MAX_SLOTS),
+                ("last_use", C.c_uint64 * WKV_TIER_MAX_SLOTS), ("clock", C.c_uint64)]
+
+
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
 
@@ -76,8 +84,16 @@ _compress = _sig("wkv_compress_chunk", C.c_int,
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
                    _SZ, _P])
+_pose_host = _sig("wkv_pose_topk_host", C.c_int,
+                  [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P])
 _pose_so3 = _sig("wkv_pose_topk_so3", C.c_int,
                  [_P, _I32, C.POINTER(wkv_pose_q), _I32, _P, _P, _P])
+_tier_init = _sig("wkv_tier_init", C.c_int, [C.POINTER(wkv_tier), _I32])
+_tier_plan = _sig("wkv_tier_plan", C.c_int, [C.POINTER(wkv_tier), _P, _I32, _P, _P, _P, _P])
+_tier_prefetch = _sig("wkv_tier_prefetch", C.c_int,
+                      [C.POINTER(wkv_tier), _P, _I32, C.POINTER(wkv_bank), C.POINTER(wkv_bank),
+                       _I32, _I32, _P, _P, _P, _P])
+_tier_resolve = _sig("wkv_tier_resolve", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P])
 _mean_ws = _sig("wkv_mean_rows_workspace_bytes", _SZ, [_I32] * 4)
 _mean_rows = _sig("wkv_mean_rows", C.c_int,
                   [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _SZ, _P])
@@ -95,7 +111,8 @@ _attn = _sig("wkv_chunk_attention", C.c_int,
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
-           "wkv_pose_topk_so3",
+           "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
+           "wkv_tier_resolve",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
 
 
@@ -236,6 +253,27 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
     return (*outs, scores)
 
 
+def wkv_pose_topk_host(bank_poses, query_hist, k: int):
+    """Pose top-k on the host, for planning (the host tier's prefetch).
+    bank_poses: float32 [M, 4] host array or CPU tensor; query_hist: one pose
+    or [prev, last]. Returns (idx int32 [k_eff], dist float64 [k_eff]) numpy."""
+    import numpy as np
+    P = np.ascontiguousarray(np.asarray(bank_poses, dtype=np.float32))
+    if P.ndim != 2 or P.shape[1] != 4:
+        raise TypeError("bank_poses: expected float32 [M, 4]")
+    M = P.shape[0]
+    hist = list(query_hist)
+    if len(hist) == 4 and not hasattr(hist[0], "__len__"):
+        hist = [hist]
+    arr = (wkv_pose * max(len(hist), 1))(*[_pose_tuple(p) for p in hist])
+    k_eff = min(int(k), M) if k >= 1 else 1
+    idx = np.empty(max(k_eff, 1), dtype=np.int32)
+    dist = np.empty(max(k_eff, 1), dtype=np.float64)
+    st = _pose_host(P.ctypes.data, M, arr, len(hist), int(k), idx.ctypes.data, dist.ctypes.data)
+    _check("wkv_pose_topk_host", st)
+    return idx[:k_eff], dist[:k_eff]
+
+
 def wkv_pose_topk_so3(poses: torch.Tensor, query, k: int, want_dist: bool = True,
                       out_idx=None, out_dist=None, stream=None):
     """Pose top-k with full rotations. poses: float32 [M, 8] device tensor
@@ -256,6 +294,69 @@ def wkv_pose_topk_so3(poses: torch.Tensor, query, k: int, want_dist: bool = True
     st = _pose_so3(_ptr(poses), M, C.byref(qs), k, _ptr(out_idx), _ptr(out_dist), _stream(stream))
     _check("wkv_pose_topk_so3", st)
     return out_idx[:k_eff], (out_dist[:k_eff] if out_dist is not None else None)
+
+
+def _bank_struct(bank) -> wkv_bank:
+    int4 = bank.get("k_scale") is not None
+    bk = wkv_bank(WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16, int(bank["k"].shape[0]),
+                  int(bank["k"].shape[1]), bank["k"].data_ptr(), bank["v"].data_ptr(),
+                  bank["k_scale"].data_ptr() if int4 else None,
+                  bank["v_scale"].data_ptr() if int4 else None)
+    return bk
+
+
+class Tier:
+    """Host-side staging table of the host tier (the library keeps no state;
+    this object owns the wkv_tier struct)."""
+
+    def __init__(self, n_slots: int):
+        self.t = wkv_tier()
+        _check("wkv_tier_init", _tier_init(C.byref(self.t), n_slots))
+
+    @property
+    def slot_chunk(self):
+        return [int(self.t.chunk[i]) for i in range(self.t.n_slots)]
+
+    def plan(self, ids):
+        """Plan a request on the host only. Returns (slot_of, [(id, slot), ...])."""
+        n = len(ids)
+        arr = (C.c_int32 * max(n, 1))(*ids)
+        so, ci, cs = (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))()
+        nc = C.c_int32(0)
+        _check("wkv_tier_plan", _tier_plan(C.byref(self.t), C.cast(arr, _P), n, C.cast(so, _P),
+                                           C.cast(ci, _P), C.cast(cs, _P), C.byref(nc)))
+        return list(so[:n]), list(zip(ci[:nc.value], cs[:nc.value]))
+
+    def prefetch(self, ids, host_bank, staging, H: int, D: int, dev_slot_chunk, dev_pred_slot,
+                 stream=None) -> int:
+        """Plan a request and enqueue the copies host bank -> staging slots and
+        the device table update on `stream`. host_bank / staging: dicts like
+        the bank of wkv_assemble_window. Returns the number of chunks copied."""
+        n = len(ids)
+        arr = (C.c_int32 * max(n, 1))(*ids)
+        hb, sb = _bank_struct(host_bank), _bank_struct(staging)
+        nc = C.c_int32(0)
+        st = _tier_prefetch(C.byref(self.t), C.cast(arr, _P), n, C.byref(hb), C.byref(sb), H, D,
+                            _ptr(dev_slot_chunk), _ptr(dev_pred_slot), C.byref(nc),
+                            _stream(stream))
+        _check("wkv_tier_prefetch", st)
+        return nc.value
+
+
+def wkv_tier_resolve(actual_idx: torch.Tensor, slot_chunk: torch.Tensor, pred_slot: torch.Tensor,
+                     out_slot=None, out_miss=None, stream=None):
+    """Staging slot of every retrieved chunk (stale predicted slot on a miss).
+    All int32 device tensors. Returns (out_slot [n], out_miss [1])."""
+    n = int(actual_idx.shape[0])
+    dev = actual_idx.device
+    if out_slot is None:
+        out_slot = torch.empty((n,), dtype=torch.int32, device=dev)
+    if out_miss is None:
+        out_miss = torch.empty((1,), dtype=torch.int32, device=dev)
+    st = _tier_resolve(_ptr(actual_idx), n, _ptr(slot_chunk), int(slot_chunk.shape[0]),
+                       _ptr(pred_slot), _ptr(out_slot), _ptr(out_miss), _stream(stream))
+    _check("wkv_tier_resolve", st)
+    return out_slot, out_miss
 
 
 def wkv_mean_rows_workspace_bytes(B: int, L: int, H: int, D: int) -> int:

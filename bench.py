@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--score-mode", default="position", choices=["position", "anchor_mean"],
                     help="compression score: cosine to the anchor key at the same position "
                          "(default) or the mean cosine to every anchor key")
+    ap.add_argument("--tier", action="store_true",
+                    help="keep the bank in pinned host memory and stage retrieved chunks into "
+                         "HBM slots from the extrapolated pose (host tier)")
     ap.add_argument("--store", default="bf16", choices=["bf16", "int4"],
                     help="format of the compressed rows in the sweep")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
@@ -150,6 +153,9 @@ def main():
     dev = torch.device("cuda:0")
     if a.config == "sweep":
         sweep(a, torch, w, S, dev)
+        return
+    if a.tier:
+        tier_bench(a, torch, w, S, dev)
         return
     c = dict(CONFIGS[a.config])
     if a.r is not None:
@@ -493,6 +499,240 @@ def sweep(a, torch, w, S, dev):
         "roofline": {"kernel": "wkv_compress_chunk (score + select + gather)", "bound": "hbm",
                      "achieved": main_cell["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": main_cell["frac"], "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def tier_bench(a, torch, w, S, dev):
+    """The hot path with the bank in pinned host memory (WorldPager: int4
+    store in pinned DRAM, next retrieval set staged from the extrapolated
+    pose, stale reuse on a miss). Per chunk step t on the compute stream:
+    compress, wait for the staging of step t, pose top-k on the true pose,
+    resolve against the staged slots, assemble from the staging bank,
+    attention. The host plans step t + 1's set from the extrapolated pose
+    (the pose is known before compute) and queues the copies of the chunks
+    not yet staged on a copy stream, after step t's assembly, so they overlap
+    step t's attention. The query
+    walks back along the bank's own trajectory (a revisit). The same steps
+    with the bank resident in HBM and direct retrieval are timed beside it."""
+    c = dict(CONFIGS[a.config])
+    if a.r is not None:
+        c["r"] = a.r
+    seed = CFG_SEED[a.config]
+    H, D, T, F, r = c["H"], c["D"], c["T"], c["F"], c["r"]
+    FT = F * T
+    Lc = T + w.wkv_keep_count(F, T, r)
+    M, k, nrec, nsteps = c["M"], c["k"], c["n_recent"], c["S"]
+    Nq, Nk = FT, FT + k * Lc + nrec * FT + FT
+    n_slots = 2 * k + 2
+    # compute and copy streams (both at the default priority)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        if c["int4"]:
+            kp, vp, ksc, vsc = S.int4_bank(seed, M, Lc, H, D, device=dev)
+            bank = {"k": kp, "v": vp, "k_scale": ksc, "v_scale": vsc}
+        else:
+            bk = torch.empty((M, Lc, H, D), dtype=torch.bfloat16, device=dev)
+            bv = torch.empty_like(bk)
+            for m in range(M):
+                bk[m], bv[m] = S.segment_kv(seed, 100 + m, Lc, H, D, device=dev)
+            bank = {"k": bk, "v": bv}
+        torch.cuda.synchronize()
+        host = {n: torch.empty(t.shape, dtype=t.dtype, pin_memory=True).copy_(t)
+                for n, t in bank.items()}
+        staging = {n: torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+                   for n, t in bank.items()}
+        chunk_bytes = sum(t[0].numel() * t.element_size() for t in host.values())
+        walk = S.pose_walk(seed, M + 3)
+        poses = walk[1:M + 1].contiguous().to(dev)
+        nstep_all = a.warmup + a.steps + 2
+        # a smooth revisit: a 5-point moving average of the bank's own path,
+        # walked backwards (and forwards again at the ends)
+        path = walk[1:M + 1].double()
+        sm = torch.stack([path[max(0, i - 2):i + 3].mean(0) for i in range(M)]).float()
+        order = list(range(M - 1, -1, -1)) + list(range(1, M - 1))
+        traj = [sm[order[t % len(order)]].tolist() for t in range(nstep_all + 1)]
+        ck, cv = S.chunk_kv(seed, 1000, 0, F, T, H, D, device=dev)
+        segs = [S.segment_kv(seed, 2000 + j, FT, H, D, device=dev) for j in range(nrec + 2)]
+        qs = [S.queries(seed, s_, Nq, H, D, device=dev) for s_ in range(nsteps)]
+        ko = torch.empty((Lc, H, D), dtype=torch.bfloat16, device=dev)
+        vo = torch.empty_like(ko)
+        kidx = torch.empty((Lc,), dtype=torch.int32, device=dev)
+        wk = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev)
+        wv = torch.empty_like(wk)
+        out = torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)
+        cws = torch.empty(max(w.wkv_compress_workspace_bytes(1, F, T, H, D), 16),
+                          dtype=torch.uint8, device=dev)
+        aws = torch.empty(max(w.wkv_attention_workspace_bytes(Nq, Nk, H, D), 16),
+                          dtype=torch.uint8, device=dev)
+        dsc = torch.empty((n_slots,), dtype=torch.int32, device=dev)
+        dps = torch.empty((64,), dtype=torch.int32, device=dev)
+        slots = torch.empty((k,), dtype=torch.int32, device=dev)
+        miss = torch.empty((1,), dtype=torch.int32, device=dev)
+        tier = w.Tier(n_slots)
+        torch.cuda.synchronize()
+
+    stats = {"copies": 0, "misses": [], "stall": [], "att": []}
+
+    poses_host = walk[1:M + 1].contiguous().numpy()
+    import ctypes as C
+    host_b, stg_bank_b = w._bank_struct(host), w._bank_struct(staging)
+    hist_arr = (w.wkv_pose * 2)()
+    ids_arr = (C.c_int32 * max(k, 1))()
+    n_cp = C.c_int32(0)
+    k_eff = min(k, M)
+
+    def stage(hist, after, timed):
+        """Plan the staging set of the next chunk on the host from its
+        extrapolated pose (the pose is known before compute), and enqueue its
+        copies on the copy stream once `after` (the last reader of the staging
+        bank) has passed; returns the event that marks the staging done."""
+        for i_, p_ in enumerate(hist):
+            hist_arr[i_].x, hist_arr[i_].y, hist_arr[i_].z, hist_arr[i_].yaw = p_
+        st_ = w._pose_host(poses_host.ctypes.data, M, hist_arr, len(hist), k,
+                           C.cast(ids_arr, C.c_void_p), None)
+        if st_ != 0:
+            raise RuntimeError(w.wkv_last_error())
+        xs.wait_event(after)
+        st_ = w._tier_prefetch(C.byref(tier.t), C.cast(ids_arr, C.c_void_p), k_eff,
+                               C.byref(host_b), C.byref(stg_bank_b), H, D,
+                               C.c_void_p(dsc.data_ptr()), C.c_void_p(dps.data_ptr()),
+                               C.byref(n_cp), C.c_void_p(xs.cuda_stream))
+        if st_ != 0:
+            raise RuntimeError(w.wkv_last_error())
+        if timed:
+            stats["copies"] += n_cp.value
+        ready = torch.cuda.Event()
+        ready.record(xs)
+        return ready
+
+    # Prepared C calls: the step's arguments are marshalled once, so the host
+    # cost per step is the library's, not the Python wrappers' (the staging
+    # path must enqueue each step behind a host decision, so it cannot run
+    # many steps ahead of the GPU as the resident path does).
+    P = C.c_void_p
+    cs_h, xs_h = P(cs.cuda_stream), P(xs.cuda_stream)
+    idx = torch.empty((k,), dtype=torch.int32, device=dev)
+    qpose = (w.wkv_pose * 1)()
+    sk_, cur_ = w._seg(segs[0]), w._seg(segs[-1])
+    rec_ = (w.wkv_segment * max(nrec, 1))(*[w._seg(p_) for p_ in segs[1:1 + nrec]])
+    stg_b, bank_b = w._bank_struct(staging), w._bank_struct(bank)
+    comp_args = (P(ck.data_ptr()), P(cv.data_ptr()), 1, F, T, H, D, float(r), 0,
+                 P(ko.data_ptr()), P(vo.data_ptr()), P(kidx.data_ptr()), None,
+                 P(cws.data_ptr()), cws.numel(), cs_h)
+    attn_args = [(P(qs[j].data_ptr()), P(wk.data_ptr()), P(wv.data_ptr()), Nq, Nk, H, D, 0.0,
+                  P(out.data_ptr()), None, P(aws.data_ptr()), aws.numel(), cs_h)
+                 for j in range(nsteps)]
+
+    def call(f, *args):
+        st_ = f(*args)
+        if st_ != 0:
+            raise RuntimeError(w.wkv_last_error())
+
+    def set_pose(p_):
+        qpose[0].x, qpose[0].y, qpose[0].z, qpose[0].yaw = p_
+
+    def step_tier(t, ready, timed):
+        """Enqueue step t, then the staging for t + 1 (no host wait)."""
+        tev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        call(w._compress, *comp_args)
+        if timed:
+            tev[0].record(cs)
+        cs.wait_event(ready)
+        if timed:
+            tev[1].record(cs)
+        set_pose(traj[t])
+        call(w._pose_topk, P(poses.data_ptr()), M, qpose, 1, k, P(idx.data_ptr()), None, None,
+             cs_h)
+        call(w._tier_resolve, P(idx.data_ptr()), min(k, M), P(dsc.data_ptr()), n_slots,
+             P(dps.data_ptr()), P(slots.data_ptr()), P(miss.data_ptr()), cs_h)
+        call(w._assemble, C.byref(sk_), C.byref(stg_b), P(slots.data_ptr()), min(k, M), rec_,
+             nrec, C.byref(cur_), H, D, P(wk.data_ptr()), P(wv.data_ptr()), Nk, cs_h)
+        if timed:
+            with torch.cuda.stream(cs):
+                stats["misses"].append(miss.clone())
+        asm = torch.cuda.Event()
+        asm.record(cs)
+        for j in range(nsteps):
+            if timed and j == 0:
+                tev[2].record(cs)
+            call(w._attn, *attn_args[j])
+        if timed:
+            tev[3].record(cs)
+            stats["stall"].append(tev)
+        # the pose of step t + 1 extrapolated from those of steps t - 1 and t
+        hist = [traj[t - 1], traj[t]] if t > 0 else [traj[t]]
+        return stage(hist, asm, timed)
+
+    def step_hbm(t):
+        call(w._compress, *comp_args)
+        set_pose(traj[t])
+        call(w._pose_topk, P(poses.data_ptr()), M, qpose, 1, k, P(idx.data_ptr()), None, None,
+             cs_h)
+        call(w._assemble, C.byref(sk_), C.byref(bank_b), P(idx.data_ptr()), min(k, M), rec_,
+             nrec, C.byref(cur_), H, D, P(wk.data_ptr()), P(wv.data_ptr()), Nk, cs_h)
+        for j in range(nsteps):
+            call(w._attn, *attn_args[j])
+
+    # step 0's set is staged from its own pose before the loop
+    ready = stage([traj[0]], torch.cuda.Event(), False)
+    for t in range(a.warmup):
+        ready = step_tier(t, ready, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    host_s = 0.0
+    for t in range(a.warmup, a.warmup + a.steps):
+        h0 = time.perf_counter()
+        ready = step_tier(t, ready, True)
+        host_s += time.perf_counter() - h0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    for t in range(a.warmup):
+        step_hbm(t)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for t in range(a.warmup, a.warmup + a.steps):
+        step_hbm(t)
+    torch.cuda.synchronize()
+    wall_hbm = time.perf_counter() - t1
+
+    stall_us = [e[0].elapsed_time(e[1]) * 1e3 for e in stats["stall"]]
+    att_ms = statistics.fmean(e[2].elapsed_time(e[3]) for e in stats["stall"]) / nsteps
+    misses = sum(int(m.item()) for m in stats["misses"])
+    flops = 4.0 * Nq * Nk * D * H
+    att_tflops = flops / (att_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(a.steps / wall, 3),
+        "unit": "chunk-steps/s (one step = compress + pose top-k + tier resolve + assemble from "
+                f"HBM staging + {nsteps} attention pass{'es' if nsteps > 1 else ''}; staging "
+                "copies overlap the attention)",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded bank and queries; the query pose walks back along the bank's "
+                "own trajectory)",
+        "config": {"workload": c["name"] + f"; bank in pinned host memory, staged through "
+                                           f"{n_slots} HBM slots", "heads": H, "head_dim": D,
+                   "stored_chunks": M, "retrieved": k, "staging_slots": n_slots,
+                   "int4_bank": c["int4"], "window_keys": Nk, "queries": Nq,
+                   "parallelism": "none"},
+        "breakdown": {
+            "hbm_resident_ms_per_step": round(wall_hbm / a.steps * 1e3, 4),
+            "host_enqueue_ms_per_step": round(host_s / a.steps * 1e3, 4),
+            "chunks_copied_per_step": round(stats["copies"] / a.steps, 3),
+            "copy_MB_per_step": round(stats["copies"] * chunk_bytes / a.steps / 1e6, 3),
+            "miss_rate": round(misses / (a.steps * min(k, M)), 4),
+            "stall_us_mean": round(statistics.fmean(stall_us), 2),
+            "stall_us_max": round(max(stall_us), 2),
+            "attention_us": round(att_ms * 1e3, 2),
+        },
+        "roofline": {"kernel": "wkv_chunk_attention", "bound": "mfma",
+                     "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)

@@ -204,6 +204,15 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
                          int32_t* out_idx, double* out_dist,
                          wkv_pose* out_query, wkv_stream_t stream);
 
+/* [host] wkv_pose_topk evaluated on the host, for planning: the host tier
+ * chooses the next chunk's staging set from the extrapolated pose while the
+ * GPU still works on the current chunk ([WorldPager] Fig. 2: the pose is an
+ * input known before compute). Same float64 operation sequence, result and
+ * order as wkv_pose_topk; bank_poses, query_hist, out_idx [min(k, M)] and
+ * out_dist (NULL ok) are host memory. */
+wkv_status wkv_pose_topk_host(const wkv_pose* bank_poses, int32_t M, const wkv_pose* query_hist,
+                              int32_t n_hist, int32_t k, int32_t* out_idx, double* out_dist);
+
 /* Pose top-k with full rotations: as wkv_pose_topk with the rotation term
  *   dr_i = 2 * atan2(|r_xyz|, |r_w|),  r = conj(q_i) * q_query
  * (the SO(3) geodesic angle, float64 from the float32 values), min-max
@@ -253,6 +262,67 @@ wkv_status wkv_mean_rows(const uint16_t* x, int32_t B, int32_t L_in, const int32
 wkv_status wkv_query_topk(const double* key_means, int32_t M, const double* query_mean,
                           int32_t H, int32_t D, int32_t k, int32_t* out_idx, double* scores,
                           wkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Host tier ([WorldKV] Sec. 4.2: evicted chunks are stored in GPU/CPU
+ * memory; [WorldPager] abstract and Fig. 2: the int4 store lives in pinned
+ * host memory, the next chunk's retrieval set is staged from the
+ * extrapolated pose, and a retrieved chunk that is not staged is replaced
+ * by staged data instead of stalling).
+ *
+ * A staging bank in HBM (a wkv_bank of n_slots chunks, same dtype and Lc as
+ * the host bank) holds the chunks most recently requested. The table below
+ * lives on the host and is owned by the caller; the library keeps no state.
+ * Planning rule: the request gets a new stamp; an id already staged keeps
+ * its slot; each other id, in request order, takes the slot with the
+ * smallest (last-use stamp, slot index) among the slots holding no id of
+ * the request, and is copied there.
+ * ------------------------------------------------------------------------ */
+
+#define WKV_TIER_MAX_SLOTS 64
+
+typedef struct {
+  int32_t n_slots;
+  int32_t chunk[WKV_TIER_MAX_SLOTS];       /* chunk id held by each slot, -1 = empty */
+  uint64_t last_use[WKV_TIER_MAX_SLOTS];   /* stamp of the last request using it, 0 = never */
+  uint64_t clock;                          /* last stamp handed out */
+} wkv_tier;
+
+/* [host] Empty table of n_slots (1..WKV_TIER_MAX_SLOTS) slots. */
+wkv_status wkv_tier_init(wkv_tier* t, int32_t n_slots);
+
+/* [host] Plan a request without copying: ids (host, distinct, 1 <= n <=
+ * n_slots, each >= 0). Writes slot_of[n], and the chunks to copy as
+ * copy_ids / copy_slots [*n_copies] (host arrays of n entries). Updates t. */
+wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* slot_of,
+                         int32_t* copy_ids, int32_t* copy_slots, int32_t* n_copies);
+
+/* Plan a request and enqueue on `stream`, in order: the copies of the
+ * chunks it needs from host_bank into their staging slots (one kernel that
+ * reads the host bank through its device mapping, so the stream's earlier
+ * waits never block the host; host_bank must be pinned host memory from
+ * hipHostMalloc, else WKV_ERR_UNSUPPORTED; ids < host_bank->M), then a
+ * small kernel writing the table's chunk
+ * ids to dev_slot_chunk [n_slots] and each id's slot to dev_pred_slot [n]
+ * (device; values captured at enqueue). The caller orders `stream` after
+ * the last reader of the staging bank and its readers after this call's
+ * work (events). *n_copies (host) receives the number of chunks copied.
+ * staging->M must equal t->n_slots. */
+wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n,
+                             const wkv_bank* host_bank, const wkv_bank* staging, int32_t H,
+                             int32_t D, int32_t* dev_slot_chunk, int32_t* dev_pred_slot,
+                             int32_t* n_copies, wkv_stream_t stream);
+
+/* For each retrieved chunk actual_idx[j] (device, j < n <= 64): out_slot[j]
+ * = the slot of slot_chunk [n_slots] holding it (a hit). The misses (a
+ * negative id is one), in rank order, take the entries of pred_slot [n]
+ * (the predicted request's slots, rank order) that no hit uses, so a chunk
+ * is never placed twice and the window never waits for a copy.
+ * out_miss[0] = number of misses (device; NULL ok). out_slot then indexes
+ * the staging bank in wkv_assemble_window. */
+wkv_status wkv_tier_resolve(const int32_t* actual_idx, int32_t n, const int32_t* slot_chunk,
+                            int32_t n_slots, const int32_t* pred_slot, int32_t* out_slot,
+                            int32_t* out_miss, wkv_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Window assembly ([WorldKV] Sec. 4.2: retrieved KV is inserted back into the
