@@ -20,8 +20,8 @@
 //            divides by T. The mean of the cosines to every anchor token
 //            is then one dot product, <k, abar> / |k|, so the score kernel
 //            reads only the non-anchor rows and abar (kept in LDS).
-//   select - one block per unit, sized to the pooled count (256, 512 or 1024
-//            threads, 8 keys each): radix select of the n_keep-th smallest
+//   select - one block per unit, sized to the pooled count (512 threads x 4
+//            keys, 1024 x 4 or 1024 x 8): radix select of the n_keep-th smallest
 //            (score, index) key, stable compaction by block scan, writes
 //            kept_idx.
 //   gather - one wave per output row: copies the kept K rows (non-anchor) and
@@ -395,10 +395,12 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
   }
 }
 
-constexpr int kSelKPT = 8;  // N <= 8 * block size
+// Select block: 512 threads with 4 keys each up to 2048 pooled tokens (short
+// per-thread chains in the histogram passes: 11.3 us against 14.6 us for 256
+// threads x 8 keys on one 1760-token unit), 1024 x 4 and 1024 x 8 beyond.
 
 // grid: B. Writes kept_idx[b][0..Lc).
-template <int kSelBlock>
+template <int kSelBlock, int kSelKPT>
 __global__ __launch_bounds__(kSelBlock) void compress_select_kernel(
     const double* __restrict__ scores, int N, int T, int n_keep,
     int32_t* __restrict__ kept_idx, int Lc) {
@@ -582,14 +584,14 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                    : dispatch_score_F<64>(k, B, F, T, H, TT, scores, out, q4, Lc, abar, s);
     if (e != hipSuccess) return e;
   }
-  if (N <= 256 * kSelKPT)
-    hipLaunchKernelGGL((compress_select_kernel<256>), dim3(B), dim3(256), 0, s, scores, N, T,
+  if (N <= 2048)
+    hipLaunchKernelGGL((compress_select_kernel<512, 4>), dim3(B), dim3(512), 0, s, scores, N, T,
                        n_keep, kept_idx, Lc);
-  else if (N <= 512 * kSelKPT)
-    hipLaunchKernelGGL((compress_select_kernel<512>), dim3(B), dim3(512), 0, s, scores, N, T,
+  else if (N <= 4096)
+    hipLaunchKernelGGL((compress_select_kernel<1024, 4>), dim3(B), dim3(1024), 0, s, scores, N, T,
                        n_keep, kept_idx, Lc);
   else
-    hipLaunchKernelGGL((compress_select_kernel<1024>), dim3(B), dim3(1024), 0, s, scores, N, T,
+    hipLaunchKernelGGL((compress_select_kernel<1024, 8>), dim3(B), dim3(1024), 0, s, scores, N, T,
                        n_keep, kept_idx, Lc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -92,8 +92,17 @@ __global__ __launch_bounds__(256) void mean_rows_final_kernel(const double* __re
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= HD) return;
   const double* p = part + (size_t)b * nsl * HD + i;
+  // Loads of eight slices in flight, added in slice order.
   double t = 0.0;
-  for (int s = 0; s < nsl; ++s) t += p[(size_t)s * HD];
+  int s = 0;
+  for (; s + 8 <= nsl; s += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(s + u) * HD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  for (; s < nsl; ++s) t += p[(size_t)s * HD];
   out[(size_t)b * HD + i] = t / (double)L;
 }
 

@@ -4,8 +4,11 @@
 //
 // Keys live in registers, KPT per thread in blocked order (thread t holds the
 // items t*KPT .. t*KPT+KPT-1). The k-th smallest key is found by an MSB-first
-// radix select with 8-bit digits; items are then kept when their key is below
-// that threshold, plus the lowest-index items equal to it, so the kept set is
+// radix select with 8-bit digits that starts below the leading bits every
+// key shares (the block's min and max key give them): scores of one sign and
+// magnitude range share a dozen or more leading bits, and skipping them
+// halves the passes. Items are then kept when their key is below that
+// threshold, plus the lowest-index items equal to it, so the kept set is
 // exactly the k smallest (key, index) pairs.
 #pragma once
 
@@ -15,6 +18,8 @@ namespace wkv {
 
 struct SelectShared {
   uint32_t hist[256];
+  uint64_t wmin[32];
+  uint64_t wmax[32];
   int wave_tot[32];
   int bucket;
   int rank;
@@ -77,17 +82,56 @@ __device__ void block_radix_select(const uint64_t (&key)[KPT],
                                    SelectShared& sh, uint64_t* prefix_out,
                                    uint64_t* mask_out, int* rank_out) {
   const int tid = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = BLOCK / 64;
+  // Leading bits shared by every valid key.
+  uint64_t kmin = ~0ull, kmax = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (valid[i]) {
+      kmin = key[i] < kmin ? key[i] : kmin;
+      kmax = key[i] > kmax ? key[i] : kmax;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax, o, 64);
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  __syncthreads();  // wmin / wmax may still be read by a previous call
+  if (lane == 0) {
+    sh.wmin[wave] = kmin;
+    sh.wmax[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = sh.wmin[0];
+  kmax = sh.wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    kmin = sh.wmin[w] < kmin ? sh.wmin[w] : kmin;
+    kmax = sh.wmax[w] > kmax ? sh.wmax[w] : kmax;
+  }
+  const uint64_t diff = kmin ^ kmax;
+  if (diff == 0) {  // every valid key is equal: keep the k lowest indices
+    *prefix_out = kmin;
+    *mask_out = ~0ull;
+    *rank_out = k;
+    return;
+  }
+  int hi = 63 - __clzll((long long)diff);  // highest bit where keys differ
+  uint64_t mask = hi == 63 ? 0ull : ~((2ull << hi) - 1ull);
+  uint64_t prefix = kmin & mask;
   int rank = k;
 #pragma unroll 1
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;  // 8 bits, fewer in the last pass
     for (int i = tid; i < 256; i += BLOCK) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       bool m = valid[i] && ((key[i] & mask) == prefix);
-      hist_add(sh.hist, m, (uint32_t)((key[i] >> shift) & 0xFF));
+      hist_add(sh.hist, m, (uint32_t)(key[i] >> lo) & dmask);
     }
     __syncthreads();
     if (tid < 64) {
@@ -122,10 +166,11 @@ __device__ void block_radix_select(const uint64_t (&key)[KPT],
     const int bucket = sh.bucket;
     rank = sh.rank;
     const int done = sh.done;
-    prefix |= (uint64_t)bucket << shift;
-    mask |= (uint64_t)0xFF << shift;
+    prefix |= (uint64_t)bucket << lo;
+    mask |= (uint64_t)dmask << lo;
     __syncthreads();  // sh.* is rewritten by the next pass
     if (done) break;
+    hi = lo - 1;
   }
   *prefix_out = prefix;
   *mask_out = mask;
