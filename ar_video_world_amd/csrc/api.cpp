@@ -611,4 +611,14 @@ wkv_status wkv_pose_topk_host(const wkv_pose* bank_poses, int32_t M, const wkv_p
   return WKV_OK;
 }
 
+wkv_pose wkv_pose_extrapolate(wkv_pose prev, wkv_pose last) {
+  wkv_pose q;
+  const double lx = last.x, ly = last.y, lz = last.z, lyaw = last.yaw;
+  q.x = (float)(2.0 * lx - (double)prev.x);
+  q.y = (float)(2.0 * ly - (double)prev.y);
+  q.z = (float)(2.0 * lz - (double)prev.z);
+  q.yaw = (float)wrap_angle(lyaw + wrap_angle(lyaw - (double)prev.yaw));
+  return q;
+}
+
 }  // extern "C"

@@ -84,6 +84,7 @@ _compress = _sig("wkv_compress_chunk", C.c_int,
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
                    _SZ, _P])
+_pose_extrap = _sig("wkv_pose_extrapolate", wkv_pose, [wkv_pose, wkv_pose])
 _pose_host = _sig("wkv_pose_topk_host", C.c_int,
                   [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P])
 _pose_so3 = _sig("wkv_pose_topk_so3", C.c_int,
@@ -111,7 +112,7 @@ _attn = _sig("wkv_chunk_attention", C.c_int,
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
-           "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
+           "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_pose_extrapolate", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
            "wkv_tier_resolve",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
 
@@ -251,6 +252,12 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
         outs = [t[0] for t in outs]
         scores = None if scores is None else scores[0]
     return (*outs, scores)
+
+
+def wkv_pose_extrapolate(prev, last):
+    """The query pose one chunk ahead: (x, y, z, yaw) floats."""
+    q = _pose_extrap(_pose_tuple(prev), _pose_tuple(last))
+    return (q.x, q.y, q.z, q.yaw)
 
 
 def wkv_pose_topk_host(bank_poses, query_hist, k: int):

@@ -406,6 +406,11 @@ def main():
             "attention_flop": flops,
             "attention_split_keys": splits,
             "event_step_ms": round(comp_ms + pose_ms + asm_ms + att_ms * nsteps, 4),
+            "percentiles_us": {name: {"p10": round(np.percentile(v, 10) * 1e3, 2),
+                                      "p50": round(np.percentile(v, 50) * 1e3, 2),
+                                      "p90": round(np.percentile(v, 90) * 1e3, 2)}
+                               for name, v in (("compress", t_comp), ("pose_topk", t_pose),
+                                               ("assemble", t_asm), ("attention", t_att))},
             "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         },
         "roofline": {
@@ -738,6 +743,18 @@ def tier_bench(a, torch, w, S, dev):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(a, c, s, bank, poses, qhist, Nq, Nk, Lc):
     """The oracle, as it stands, on a bounded sample of one step's work."""
     import numpy as np
@@ -802,6 +819,7 @@ def cpu_baseline(a, c, s, bank, poses, qhist, Nq, Nk, Lc):
         "value": round(1.0 / t_step, 6),
         "unit": "chunk-steps/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"numpy fp64 oracle: compress of 1 unit, pose top-k over {len(P)} poses "
                    f"and window assembly ({Nk} rows) in full; attention for {rows_done} query "

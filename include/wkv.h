@@ -204,6 +204,12 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
                          int32_t* out_idx, double* out_dist,
                          wkv_pose* out_query, wkv_stream_t stream);
 
+/* [host] The query pose extrapolated one chunk ahead ([WorldPager] Fig. 2:
+ * the next retrieval set comes from the extrapolated camera pose):
+ * translation last + (last - prev), yaw wrap(yaw_l + wrap(yaw_l - yaw_p)),
+ * in float64, rounded to float. wkv_pose_topk with n_hist = 2 uses it. */
+wkv_pose wkv_pose_extrapolate(wkv_pose prev, wkv_pose last);
+
 /* [host] wkv_pose_topk evaluated on the host, for planning: the host tier
  * chooses the next chunk's staging set from the extrapolated pose while the
  * GPU still works on the current chunk ([WorldPager] Fig. 2: the pose is an

@@ -105,3 +105,14 @@ def test_host_pose_topk_seam_and_checks(w):
         w.wkv_pose_topk_host(P, [[0, 0, 0, 0]], 0)
     with pytest.raises(w.WkvError):
         w.wkv_pose_topk_host(P, [[0, 0, 0, 0]] * 3, 1)
+
+
+def test_pose_extrapolate_equals_oracle(w):
+    rng = np.random.default_rng(21)
+    for _ in range(500):
+        prev = rng.standard_normal(4).astype(np.float32) * np.float32(3)
+        last = rng.standard_normal(4).astype(np.float32) * np.float32(3)
+        prev[3] = np.float32(rng.uniform(-np.pi, np.pi))
+        last[3] = np.float32(rng.uniform(-np.pi, np.pi))
+        got = np.array(w.wkv_pose_extrapolate(prev, last), dtype=np.float32)
+        assert np.array_equal(got, O.pose_extrapolate(prev, last))
