@@ -423,21 +423,23 @@ def query_topk(key_means, query_mean, k: int):
 # a miss reuses what is staged instead of stalling)
 # ----------------------------------------------------------------------------
 
-def tier_plan(slot_chunk, last_use, clock: int, ids):
+def tier_plan(slot_chunk, last_use, clock: int, ids, keep=()):
     """Stage the chunks `ids` (distinct) into HBM slots, least recently used
     first. slot_chunk / last_use: lists over the slots (chunk -1 = empty,
-    stamp 0 = never used); clock: the last stamp handed out.
+    stamp 0 = never used); clock: the last stamp handed out; keep: chunks
+    whose slots must not be evicted by this request (e.g. still being read).
 
     The request gets stamp clock + 1. An id already held keeps its slot. Each
     other id, in request order, takes the slot with the smallest (stamp, slot
-    index) among the slots that hold no id of this request, and is copied.
-    Returns (slot_chunk, last_use, clock, slot_of, copies) with copies a list
-    of (id, slot)."""
+    index) among the slots that hold no id of this request and no kept
+    chunk, and is copied. Returns (slot_chunk, last_use, clock, slot_of,
+    copies) with copies a list of (id, slot); None when too few slots are
+    free."""
     sc = list(slot_chunk)
     lu = list(last_use)
     clock += 1
     slot_of = [-1] * len(ids)
-    taken = [False] * len(sc)
+    taken = [c >= 0 and c in keep for c in sc]
     for i, c in enumerate(ids):
         for s_, held in enumerate(sc):
             if held == c:
@@ -450,6 +452,8 @@ def tier_plan(slot_chunk, last_use, clock: int, ids):
         if slot_of[i] >= 0:
             continue
         cand = [(lu[s_], s_) for s_ in range(len(sc)) if not taken[s_]]
+        if not cand:
+            return None
         _, v = min(cand)
         sc[v] = c
         lu[v] = clock
@@ -463,8 +467,9 @@ def tier_resolve(actual, slot_chunk, pred_slot):
     """Staging slot of every retrieved chunk: the slot holding it (a hit), or
     on a miss a staged predicted chunk instead of waiting for a copy. The
     misses, in rank order, take the predicted slots (in rank order) that no
-    hit uses, so no chunk appears twice. A negative id is a miss. Returns
-    (slots, number of misses)."""
+    hit uses, so no chunk appears twice. A negative id is a miss. Distinct
+    predicted slots always leave enough spares; if they run out (repeated
+    predicted slots) the miss gets -1. Returns (slots, number of misses)."""
     hit = []
     for a in actual:
         hit.append(next((i for i, c in enumerate(slot_chunk) if a >= 0 and c == a), -1))
@@ -474,7 +479,7 @@ def tier_resolve(actual, slot_chunk, pred_slot):
         if h >= 0:
             out.append(h)
         else:
-            out.append(spare[miss])
+            out.append(spare[miss] if miss < len(spare) else -1)   # -1: spares ran out
             miss += 1
     return out, miss
 

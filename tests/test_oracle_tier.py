@@ -38,6 +38,9 @@ def test_resolve_by_hand():
     # slots 0, 2, 3; retrieved 5, 9, 3 -> hits 9 (0) and 3 (2), 5 takes 3
     slots, miss = O.tier_resolve([5, 9, 3], slot_chunk, [0, 2, 3])
     assert slots == [3, 0, 2] and miss == 1
+    # repeated predicted slots can run out of spares: the miss gets -1
+    slots, miss = O.tier_resolve([9, 4], slot_chunk, [0, 0])
+    assert slots == [0, -1] and miss == 1
 
 
 def test_resolve_never_repeats_a_slot():
@@ -73,3 +76,32 @@ def test_plan_invariants_random_streams(seed):
             assert v not in kept
             untouched = [s for s in range(S_) if s not in so]
             assert all((lu_before[v], v) < (lu_before[u], u) for u in untouched)
+
+
+def test_kept_chunks_are_not_evicted_by_hand():
+    sc, lu, clk = [5, 9, 3, 7], [4, 2, 1, 3], 4
+    # 3 (slot 2) is the oldest, but it is still being read: 8 takes slot 1
+    sc2, lu2, clk2, so, cp = O.tier_plan(sc, lu, clk, [8], keep=(3,))
+    assert so == [1] and cp == [(8, 1)] and sc2 == [5, 8, 3, 7]
+    # without the keep, slot 2 goes
+    assert O.tier_plan(sc, lu, clk, [8])[3] == [2]
+    # too few free slots: every other slot kept
+    assert O.tier_plan(sc, lu, clk, [8, 6], keep=(5, 9, 3)) is None
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_keep_invariant_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    S_ = 12
+    sc, lu, clk = [-1] * S_, [0] * S_, 0
+    for _ in range(200):
+        ids = [int(x) for x in rng.choice(40, size=4, replace=False)]
+        keep = tuple(int(x) for x in rng.choice(40, size=6, replace=False))
+        r = O.tier_plan(sc, lu, clk, ids, keep)
+        if r is None:
+            continue
+        sc2 = r[0]
+        for s_, c in enumerate(sc):
+            if c in keep:
+                assert sc2[s_] == c
+        sc, lu, clk = r[0], r[1], r[2]
