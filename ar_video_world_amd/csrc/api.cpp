@@ -270,10 +270,12 @@ wkv_status wkv_tier_init(wkv_tier* t, int32_t n_slots) {
   return WKV_OK;
 }
 
-wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* slot_of,
-                         int32_t* copy_ids, int32_t* copy_slots, int32_t* n_copies) {
-  if (!t || !ids || !slot_of || !copy_ids || !copy_slots || !n_copies)
+wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
+                         int32_t n_keep, int32_t* slot_of, int32_t* copy_ids,
+                         int32_t* copy_slots, int32_t* n_copies) {
+  if (!t || !ids || !slot_of || !copy_ids || !copy_slots || !n_copies || (n_keep > 0 && !keep_ids))
     return fail(WKV_ERR_NULL, "wkv_tier_plan: null argument");
+  if (n_keep < 0) return fail(WKV_ERR_SHAPE, "wkv_tier_plan: n_keep=%d", n_keep);
   if (t->n_slots < 1 || t->n_slots > WKV_TIER_MAX_SLOTS)
     return fail(WKV_ERR_SHAPE, "wkv_tier_plan: table not initialised (n_slots=%d)", t->n_slots);
   if (n < 1 || n > t->n_slots)
@@ -283,15 +285,20 @@ wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* sl
     for (int j = 0; j < i; ++j)
       if (ids[j] == ids[i]) return fail(WKV_ERR_SHAPE, "wkv_tier_plan: id %d repeated", ids[i]);
   }
-  const uint64_t stamp = ++t->clock;
+  // Work on a copy: a request that does not fit leaves the table unchanged.
+  wkv_tier nt = *t;
+  const uint64_t stamp = ++nt.clock;
   bool taken[WKV_TIER_MAX_SLOTS] = {};
+  for (int s = 0; s < nt.n_slots; ++s)
+    for (int j = 0; j < n_keep && !taken[s]; ++j)
+      taken[s] = nt.chunk[s] >= 0 && nt.chunk[s] == keep_ids[j];
   for (int i = 0; i < n; ++i) {
     slot_of[i] = -1;
-    for (int s = 0; s < t->n_slots; ++s)
-      if (t->chunk[s] == ids[i]) {
+    for (int s = 0; s < nt.n_slots; ++s)
+      if (nt.chunk[s] == ids[i]) {
         slot_of[i] = s;
         taken[s] = true;
-        t->last_use[s] = stamp;
+        nt.last_use[s] = stamp;
         break;
       }
   }
@@ -299,24 +306,28 @@ wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* sl
   for (int i = 0; i < n; ++i) {
     if (slot_of[i] >= 0) continue;
     int v = -1;
-    for (int s = 0; s < t->n_slots; ++s)
-      if (!taken[s] && (v < 0 || t->last_use[s] < t->last_use[v])) v = s;  // ties: lower slot
-    t->chunk[v] = ids[i];
-    t->last_use[v] = stamp;
+    for (int s = 0; s < nt.n_slots; ++s)
+      if (!taken[s] && (v < 0 || nt.last_use[s] < nt.last_use[v])) v = s;  // ties: lower slot
+    if (v < 0)
+      return fail(WKV_ERR_SHAPE, "wkv_tier_plan: %d slots cannot hold the request beside the kept chunks",
+                  nt.n_slots);
+    nt.chunk[v] = ids[i];
+    nt.last_use[v] = stamp;
     taken[v] = true;
     slot_of[i] = v;
     copy_ids[nc] = ids[i];
     copy_slots[nc] = v;
     ++nc;
   }
+  *t = nt;
   *n_copies = nc;
   return WKV_OK;
 }
 
-wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n,
-                             const wkv_bank* host_bank, const wkv_bank* staging, int32_t H,
-                             int32_t D, int32_t* dev_slot_chunk, int32_t* dev_pred_slot,
-                             int32_t* n_copies, wkv_stream_t stream) {
+wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
+                             int32_t n_keep, const wkv_bank* host_bank, const wkv_bank* staging,
+                             int32_t H, int32_t D, int32_t copy_mode, int32_t* dev_slot_chunk,
+                             int32_t* dev_pred_slot, int32_t* n_copies, wkv_stream_t stream) {
   if (!t || !ids || !host_bank || !staging || !dev_slot_chunk || !dev_pred_slot || !n_copies)
     return fail(WKV_ERR_NULL, "wkv_tier_prefetch: null argument");
   if (wkv_status st = check_hd(H, D)) return st;
@@ -333,15 +344,31 @@ wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n,
       return fail(WKV_ERR_SHAPE, "wkv_tier_prefetch: ids[%d]=%d >= M=%d", i, ids[i], host_bank->M);
   if (!aligned16(dev_slot_chunk) || !aligned16(dev_pred_slot))
     return fail(WKV_ERR_ALIGN, "wkv_tier_prefetch: device pointers must be 16-byte aligned");
+  if (copy_mode != WKV_TIER_COPY_KERNEL && copy_mode != WKV_TIER_COPY_ENGINE)
+    return fail(WKV_ERR_UNSUPPORTED, "wkv_tier_prefetch: copy_mode=%d", copy_mode);
   // Plan on a copy of the table: nothing changes unless every enqueue succeeds.
   wkv_tier nt = *t;
   int32_t slot_of[WKV_TIER_MAX_SLOTS], cid[WKV_TIER_MAX_SLOTS], cslot[WKV_TIER_MAX_SLOTS], nc = 0;
-  if (wkv_status st = wkv_tier_plan(&nt, ids, n, slot_of, cid, cslot, &nc)) return st;
+  if (wkv_status st = wkv_tier_plan(&nt, ids, n, keep_ids, n_keep, slot_of, cid, cslot, &nc))
+    return st;
   const size_t rows = (size_t)host_bank->Lc * H * D;
   const size_t kv_bytes = q4 ? rows / 2 : rows * 2;
   const size_t sc_bytes = q4 ? rows / 32 * 2 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (nc > 0) {
+  if (nc > 0 && copy_mode == WKV_TIER_COPY_ENGINE) {
+    for (int i = 0; i < nc; ++i) {
+      const size_t src = (size_t)cid[i], dst = (size_t)cslot[i];
+      const void* from[4] = {host_bank->k, host_bank->v, host_bank->k_scale, host_bank->v_scale};
+      const void* to[4] = {staging->k, staging->v, staging->k_scale, staging->v_scale};
+      for (int c = 0; c < (q4 ? 4 : 2); ++c) {
+        const size_t bytes = c < 2 ? kv_bytes : sc_bytes;
+        hipError_t e = hipMemcpyAsync(static_cast<char*>(const_cast<void*>(to[c])) + dst * bytes,
+                                      static_cast<const char*>(from[c]) + src * bytes, bytes,
+                                      hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch copy");
+      }
+    }
+  } else if (nc > 0) {
     // The copies read the host bank through its device mapping (pinned
     // memory allocated with hipHostMalloc is mapped); anything else is
     // refused here rather than touched by the kernel.

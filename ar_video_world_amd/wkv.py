@@ -90,10 +90,13 @@ _pose_host = _sig("wkv_pose_topk_host", C.c_int,
 _pose_so3 = _sig("wkv_pose_topk_so3", C.c_int,
                  [_P, _I32, C.POINTER(wkv_pose_q), _I32, _P, _P, _P])
 _tier_init = _sig("wkv_tier_init", C.c_int, [C.POINTER(wkv_tier), _I32])
-_tier_plan = _sig("wkv_tier_plan", C.c_int, [C.POINTER(wkv_tier), _P, _I32, _P, _P, _P, _P])
+_tier_plan = _sig("wkv_tier_plan", C.c_int,
+                  [C.POINTER(wkv_tier), _P, _I32, _P, _I32, _P, _P, _P, _P])
 _tier_prefetch = _sig("wkv_tier_prefetch", C.c_int,
-                      [C.POINTER(wkv_tier), _P, _I32, C.POINTER(wkv_bank), C.POINTER(wkv_bank),
-                       _I32, _I32, _P, _P, _P, _P])
+                      [C.POINTER(wkv_tier), _P, _I32, _P, _I32, C.POINTER(wkv_bank),
+                       C.POINTER(wkv_bank), _I32, _I32, _I32, _P, _P, _P, _P])
+WKV_TIER_COPY_KERNEL = 0
+WKV_TIER_COPY_ENGINE = 1
 _tier_resolve = _sig("wkv_tier_resolve", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P])
 _mean_ws = _sig("wkv_mean_rows_workspace_bytes", _SZ, [_I32] * 4)
 _mean_rows = _sig("wkv_mean_rows", C.c_int,
@@ -324,28 +327,32 @@ class Tier:
     def slot_chunk(self):
         return [int(self.t.chunk[i]) for i in range(self.t.n_slots)]
 
-    def plan(self, ids):
-        """Plan a request on the host only. Returns (slot_of, [(id, slot), ...])."""
+    def plan(self, ids, keep=()):
+        """Plan a request on the host only; chunks in `keep` are not evicted.
+        Returns (slot_of, [(id, slot), ...])."""
         n = len(ids)
         arr = (C.c_int32 * max(n, 1))(*ids)
+        kp = (C.c_int32 * max(len(keep), 1))(*keep)
         so, ci, cs = (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))()
         nc = C.c_int32(0)
-        _check("wkv_tier_plan", _tier_plan(C.byref(self.t), C.cast(arr, _P), n, C.cast(so, _P),
-                                           C.cast(ci, _P), C.cast(cs, _P), C.byref(nc)))
+        _check("wkv_tier_plan", _tier_plan(C.byref(self.t), C.cast(arr, _P), n, C.cast(kp, _P),
+                                           len(keep), C.cast(so, _P), C.cast(ci, _P),
+                                           C.cast(cs, _P), C.byref(nc)))
         return list(so[:n]), list(zip(ci[:nc.value], cs[:nc.value]))
 
     def prefetch(self, ids, host_bank, staging, H: int, D: int, dev_slot_chunk, dev_pred_slot,
-                 stream=None) -> int:
+                 keep=(), copy_mode: int = WKV_TIER_COPY_KERNEL, stream=None) -> int:
         """Plan a request and enqueue the copies host bank -> staging slots and
         the device table update on `stream`. host_bank / staging: dicts like
         the bank of wkv_assemble_window. Returns the number of chunks copied."""
         n = len(ids)
         arr = (C.c_int32 * max(n, 1))(*ids)
+        kp = (C.c_int32 * max(len(keep), 1))(*keep)
         hb, sb = _bank_struct(host_bank), _bank_struct(staging)
         nc = C.c_int32(0)
-        st = _tier_prefetch(C.byref(self.t), C.cast(arr, _P), n, C.byref(hb), C.byref(sb), H, D,
-                            _ptr(dev_slot_chunk), _ptr(dev_pred_slot), C.byref(nc),
-                            _stream(stream))
+        st = _tier_prefetch(C.byref(self.t), C.cast(arr, _P), n, C.cast(kp, _P), len(keep),
+                            C.byref(hb), C.byref(sb), H, D, copy_mode, _ptr(dev_slot_chunk),
+                            _ptr(dev_pred_slot), C.byref(nc), _stream(stream))
         _check("wkv_tier_prefetch", st)
         return nc.value
 

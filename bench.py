@@ -17,6 +17,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -74,6 +75,8 @@ def parse():
     ap.add_argument("--tier", action="store_true",
                     help="keep the bank in pinned host memory and stage retrieved chunks into "
                          "HBM slots from the extrapolated pose (host tier)")
+    ap.add_argument("--tier-copy", default="engine", choices=["engine", "kernel"],
+                    help="host tier staging copies: copy engine (default) or a copy kernel")
     ap.add_argument("--store", default="bf16", choices=["bf16", "int4"],
                     help="format of the compressed rows in the sweep")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
@@ -235,13 +238,17 @@ def main():
             step(i)
         torch.cuda.synchronize()
 
-        # ---- timed region: wall clock over exactly K steps
+        # ---- timed region: wall clock over exactly K steps (no cyclic-GC
+        # pass inside it)
+        gc.collect()
+        gc.disable()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(a.steps):
             step(i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        gc.enable()
         wall = t1 - t0
 
         # ---- per-call durations, from HIP events on the launch stream
@@ -521,6 +528,7 @@ def tier_bench(a, torch, w, S, dev):
     step t's attention. The query
     walks back along the bank's own trajectory (a revisit). The same steps
     with the bank resident in HBM and direct retrieval are timed beside it."""
+    import numpy as np
     c = dict(CONFIGS[a.config])
     if a.r is not None:
         c["r"] = a.r
@@ -530,7 +538,9 @@ def tier_bench(a, torch, w, S, dev):
     Lc = T + w.wkv_keep_count(F, T, r)
     M, k, nrec, nsteps = c["M"], c["k"], c["n_recent"], c["S"]
     Nq, Nk = FT, FT + k * Lc + nrec * FT + FT
-    n_slots = 2 * k + 2
+    # staging holds the next set beside the current retrieved and predicted sets
+    n_slots = 3 * k + 2
+    copy_mode = w.WKV_TIER_COPY_ENGINE if a.tier_copy == "engine" else w.WKV_TIER_COPY_KERNEL
     # compute and copy streams (both at the default priority)
     cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
     with torch.cuda.stream(cs):
@@ -571,10 +581,14 @@ def tier_bench(a, torch, w, S, dev):
                           dtype=torch.uint8, device=dev)
         aws = torch.empty(max(w.wkv_attention_workspace_bytes(Nq, Nk, H, D), 16),
                           dtype=torch.uint8, device=dev)
-        dsc = torch.empty((n_slots,), dtype=torch.int32, device=dev)
-        dps = torch.empty((64,), dtype=torch.int32, device=dev)
+        # device slot tables, one per step parity: the copy stream writes the
+        # next step's table while the current step may still read its own
+        dsc = [torch.empty((n_slots,), dtype=torch.int32, device=dev) for _ in range(2)]
+        dps = [torch.empty((64,), dtype=torch.int32, device=dev) for _ in range(2)]
         slots = torch.empty((k,), dtype=torch.int32, device=dev)
-        miss = torch.empty((1,), dtype=torch.int32, device=dev)
+        # misses of every step, written in place by the resolve (no per-step
+        # allocation: torch's allocator would synchronise on stream events)
+        miss = torch.zeros((nstep_all + 1, 4), dtype=torch.int32, device=dev)   # 16-byte rows
         tier = w.Tier(n_slots)
         torch.cuda.synchronize()
 
@@ -588,22 +602,32 @@ def tier_bench(a, torch, w, S, dev):
     n_cp = C.c_int32(0)
     k_eff = min(k, M)
 
-    def stage(hist, after, timed):
-        """Plan the staging set of the next chunk on the host from its
-        extrapolated pose (the pose is known before compute), and enqueue its
-        copies on the copy stream once `after` (the last reader of the staging
-        bank) has passed; returns the event that marks the staging done."""
+    pred = {}    # step -> predicted ids (host)
+
+    def host_topk(hist):
         for i_, p_ in enumerate(hist):
             hist_arr[i_].x, hist_arr[i_].y, hist_arr[i_].z, hist_arr[i_].yaw = p_
         st_ = w._pose_host(poses_host.ctypes.data, M, hist_arr, len(hist), k,
                            C.cast(ids_arr, C.c_void_p), None)
         if st_ != 0:
             raise RuntimeError(w.wkv_last_error())
-        xs.wait_event(after)
-        st_ = w._tier_prefetch(C.byref(tier.t), C.cast(ids_arr, C.c_void_p), k_eff,
-                               C.byref(host_b), C.byref(stg_bank_b), H, D,
-                               C.c_void_p(dsc.data_ptr()), C.c_void_p(dps.data_ptr()),
-                               C.byref(n_cp), C.c_void_p(xs.cuda_stream))
+        return [int(ids_arr[i_]) for i_ in range(k_eff)]
+
+    def stage(t_next, hist, keep, timed):
+        """Plan the staging set of step t_next on the host from its
+        extrapolated pose (the pose is known before compute) and enqueue its
+        copies on the copy stream. The chunks still read by enqueued steps
+        are kept, and the table goes to the buffer of t_next's parity, so the
+        copy stream waits for nothing; returns the event marking it done."""
+        ids = host_topk(hist)
+        pred[t_next] = ids
+        keep_arr = (C.c_int32 * max(len(keep), 1))(*keep)
+        st_ = w._tier_prefetch(C.byref(tier.t), C.cast((C.c_int32 * k_eff)(*ids), C.c_void_p),
+                               k_eff, C.cast(keep_arr, C.c_void_p), len(keep),
+                               C.byref(host_b), C.byref(stg_bank_b), H, D, copy_mode,
+                               C.c_void_p(dsc[t_next % 2].data_ptr()),
+                               C.c_void_p(dps[t_next % 2].data_ptr()), C.byref(n_cp),
+                               C.c_void_p(xs.cuda_stream))
         if st_ != 0:
             raise RuntimeError(w.wkv_last_error())
         if timed:
@@ -638,8 +662,10 @@ def tier_bench(a, torch, w, S, dev):
     def set_pose(p_):
         qpose[0].x, qpose[0].y, qpose[0].z, qpose[0].yaw = p_
 
+    asm_prev = [None]
+
     def step_tier(t, ready, timed):
-        """Enqueue step t, then the staging for t + 1 (no host wait)."""
+        """Enqueue step t, then plan and enqueue the staging of step t + 1."""
         tev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
         call(w._compress, *comp_args)
         if timed:
@@ -650,13 +676,12 @@ def tier_bench(a, torch, w, S, dev):
         set_pose(traj[t])
         call(w._pose_topk, P(poses.data_ptr()), M, qpose, 1, k, P(idx.data_ptr()), None, None,
              cs_h)
-        call(w._tier_resolve, P(idx.data_ptr()), min(k, M), P(dsc.data_ptr()), n_slots,
-             P(dps.data_ptr()), P(slots.data_ptr()), P(miss.data_ptr()), cs_h)
-        call(w._assemble, C.byref(sk_), C.byref(stg_b), P(slots.data_ptr()), min(k, M), rec_,
+        call(w._tier_resolve, P(idx.data_ptr()), k_eff, P(dsc[t % 2].data_ptr()), n_slots,
+             P(dps[t % 2].data_ptr()), P(slots.data_ptr()), P(miss[t].data_ptr()), cs_h)
+        call(w._assemble, C.byref(sk_), C.byref(stg_b), P(slots.data_ptr()), k_eff, rec_,
              nrec, C.byref(cur_), H, D, P(wk.data_ptr()), P(wv.data_ptr()), Nk, cs_h)
         if timed:
-            with torch.cuda.stream(cs):
-                stats["misses"].append(miss.clone())
+            stats["misses"].append(t)
         asm = torch.cuda.Event()
         asm.record(cs)
         for j in range(nsteps):
@@ -666,9 +691,16 @@ def tier_bench(a, torch, w, S, dev):
         if timed:
             tev[3].record(cs)
             stats["stall"].append(tev)
+        # Step t - 1 has finished reading the staging bank and its table
+        # buffer once its assembly is done: the host stays one step ahead.
+        if asm_prev[0] is not None:
+            asm_prev[0].synchronize()
+        asm_prev[0] = asm
+        # chunks step t may still read: its retrieved set and its prediction
+        keep = sorted(set(host_topk([traj[t]])) | set(pred.get(t, [])))
         # the pose of step t + 1 extrapolated from those of steps t - 1 and t
         hist = [traj[t - 1], traj[t]] if t > 0 else [traj[t]]
-        return stage(hist, asm, timed)
+        return stage(t + 1, hist, keep, timed)
 
     def step_hbm(t):
         call(w._compress, *comp_args)
@@ -681,10 +713,14 @@ def tier_bench(a, torch, w, S, dev):
             call(w._attn, *attn_args[j])
 
     # step 0's set is staged from its own pose before the loop
-    ready = stage([traj[0]], torch.cuda.Event(), False)
+    ready = stage(0, [traj[0]], [], False)
     for t in range(a.warmup):
         ready = step_tier(t, ready, False)
     torch.cuda.synchronize()
+    # the loop makes a few Python objects per step; a cyclic-GC pass over the
+    # large bank setup (tens of ms) would land inside the timed region
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     host_s = 0.0
     for t in range(a.warmup, a.warmup + a.steps):
@@ -702,10 +738,14 @@ def tier_bench(a, torch, w, S, dev):
         step_hbm(t)
     torch.cuda.synchronize()
     wall_hbm = time.perf_counter() - t1
+    gc.enable()
 
     stall_us = [e[0].elapsed_time(e[1]) * 1e3 for e in stats["stall"]]
+    # step period on the compute stream, from one step's compression to the
+    # next: its median is robust to a rare host hiccup in the wall clock
+    period_ms = [a_[0].elapsed_time(b_[0]) for a_, b_ in zip(stats["stall"], stats["stall"][1:])]
     att_ms = statistics.fmean(e[2].elapsed_time(e[3]) for e in stats["stall"]) / nsteps
-    misses = sum(int(m.item()) for m in stats["misses"])
+    misses = int(miss[stats["misses"], 0].sum().item())
     flops = 4.0 * Nq * Nk * D * H
     att_tflops = flops / (att_ms * 1e-3) / 1e12
     rec = {
@@ -720,11 +760,16 @@ def tier_bench(a, torch, w, S, dev):
         "data": "synthetic (seeded bank and queries; the query pose walks back along the bank's "
                 "own trajectory)",
         "config": {"workload": c["name"] + f"; bank in pinned host memory, staged through "
-                                           f"{n_slots} HBM slots", "heads": H, "head_dim": D,
+                                           f"{n_slots} HBM slots by {a.tier_copy} copies",
+                   "heads": H, "head_dim": D, "tier_copy": a.tier_copy,
                    "stored_chunks": M, "retrieved": k, "staging_slots": n_slots,
                    "int4_bank": c["int4"], "window_keys": Nk, "queries": Nq,
                    "parallelism": "none"},
         "breakdown": {
+            "step_period_ms_p50": round(float(np.percentile(period_ms, 50)), 4),
+            "step_period_ms_p90": round(float(np.percentile(period_ms, 90)), 4),
+            "step_period_ms_max": round(max(period_ms), 4),
+            "step_period_argmax": int(np.argmax(period_ms)),
             "hbm_resident_ms_per_step": round(wall_hbm / a.steps * 1e3, 4),
             "host_enqueue_ms_per_step": round(host_s / a.steps * 1e3, 4),
             "chunks_copied_per_step": round(stats["copies"] / a.steps, 3),

@@ -298,26 +298,40 @@ typedef struct {
 wkv_status wkv_tier_init(wkv_tier* t, int32_t n_slots);
 
 /* [host] Plan a request without copying: ids (host, distinct, 1 <= n <=
- * n_slots, each >= 0). Writes slot_of[n], and the chunks to copy as
- * copy_ids / copy_slots [*n_copies] (host arrays of n entries). Updates t. */
-wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, int32_t* slot_of,
-                         int32_t* copy_ids, int32_t* copy_slots, int32_t* n_copies);
+ * n_slots, each >= 0). keep_ids [n_keep] (host, NULL when 0) name chunks
+ * whose slots must not be evicted, because an enqueued chunk still reads
+ * them. Writes slot_of[n], and the chunks to copy as copy_ids / copy_slots
+ * [*n_copies] (host arrays of n entries). Updates t; a request that cannot
+ * fit beside the kept chunks is WKV_ERR_SHAPE and changes nothing. */
+wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
+                         int32_t n_keep, int32_t* slot_of, int32_t* copy_ids,
+                         int32_t* copy_slots, int32_t* n_copies);
 
-/* Plan a request and enqueue on `stream`, in order: the copies of the
- * chunks it needs from host_bank into their staging slots (one kernel that
- * reads the host bank through its device mapping, so the stream's earlier
- * waits never block the host; host_bank must be pinned host memory from
- * hipHostMalloc, else WKV_ERR_UNSUPPORTED; ids < host_bank->M), then a
- * small kernel writing the table's chunk
+/* How wkv_tier_prefetch moves chunks.
+ *   WKV_TIER_COPY_KERNEL: one kernel reads the pinned host bank through its
+ *     device mapping (host_bank must come from hipHostMalloc). It waits on
+ *     the device for anything ordered before it on `stream`, but holds a few
+ *     CUs while it runs.
+ *   WKV_TIER_COPY_ENGINE: copy-engine transfers (hipMemcpyAsync), no CUs.
+ *     Use it on a stream with no waits on other streams' events (order the
+ *     staging by keep_ids and double-buffered tables instead): otherwise the
+ *     runtime may block the host until those events complete. */
+enum { WKV_TIER_COPY_KERNEL = 0, WKV_TIER_COPY_ENGINE = 1 };
+
+/* Plan a request (as wkv_tier_plan, with keep_ids) and enqueue on `stream`,
+ * in order: the copies of the chunks it needs from host_bank (pinned host
+ * memory; ids < host_bank->M) into their staging slots, by copy_mode (a
+ * kernel copy needs a device mapping of host_bank, else
+ * WKV_ERR_UNSUPPORTED), then a small kernel writing the table's chunk
  * ids to dev_slot_chunk [n_slots] and each id's slot to dev_pred_slot [n]
  * (device; values captured at enqueue). The caller orders `stream` after
  * the last reader of the staging bank and its readers after this call's
  * work (events). *n_copies (host) receives the number of chunks copied.
  * staging->M must equal t->n_slots. */
-wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n,
-                             const wkv_bank* host_bank, const wkv_bank* staging, int32_t H,
-                             int32_t D, int32_t* dev_slot_chunk, int32_t* dev_pred_slot,
-                             int32_t* n_copies, wkv_stream_t stream);
+wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
+                             int32_t n_keep, const wkv_bank* host_bank, const wkv_bank* staging,
+                             int32_t H, int32_t D, int32_t copy_mode, int32_t* dev_slot_chunk,
+                             int32_t* dev_pred_slot, int32_t* n_copies, wkv_stream_t stream);
 
 /* For each retrieved chunk actual_idx[j] (device, j < n <= 64): out_slot[j]
  * = the slot of slot_chunk [n_slots] holding it (a hit). The misses (a

@@ -49,7 +49,8 @@ def same(a, b):
 
 
 @pytest.mark.parametrize("int4", [False, True])
-def test_prefetch_stream_stages_exact_chunks(w, int4):
+@pytest.mark.parametrize("copy_mode", [0, 1])
+def test_prefetch_stream_stages_exact_chunks(w, int4, copy_mode):
     M, Lc, H, D, n_slots = 30, 96, 4, 128, 8
     hb = host_bank(int4, M, Lc, H, D)
     st = staging_like(hb, n_slots)
@@ -63,9 +64,11 @@ def test_prefetch_stream_stages_exact_chunks(w, int4):
     for step in range(25):
         n = int(rng.integers(1, 5))
         ids = [int(x) for x in rng.choice(12, size=n, replace=False)]   # a small working set: reuse
-        say("tier_prefetch", int4, step, ids)
-        nc = t.prefetch(ids, hb, st, H, D, dsc, dps, stream=stream)
-        osc, olu, oclk, oso, ocp = O.tier_plan(osc, olu, oclk, ids)
+        keep = [int(x) for x in rng.choice(12, size=2, replace=False)]
+        say("tier_prefetch", int4, copy_mode, step, ids, keep)
+        nc = t.prefetch(ids, hb, st, H, D, dsc, dps, keep=keep, copy_mode=copy_mode,
+                        stream=stream)
+        osc, olu, oclk, oso, ocp = O.tier_plan(osc, olu, oclk, ids, tuple(keep))
         assert nc == len(ocp)
         total += nc
         stream.synchronize()
@@ -99,7 +102,8 @@ def test_resolve_matches_oracle(w):
 
 
 @pytest.mark.parametrize("int4", [False, True])
-def test_window_from_staging_equals_oracle(w, int4):
+@pytest.mark.parametrize("copy_mode", [0, 1])
+def test_window_from_staging_equals_oracle(w, int4, copy_mode):
     """Predicted set staged, actual set resolved (with a miss), window
     assembled from the staging bank, against the oracle window over the host
     bank's resolved chunks."""
@@ -109,10 +113,10 @@ def test_window_from_staging_equals_oracle(w, int4):
     t = w.Tier(n_slots)
     dsc = torch.empty((n_slots,), dtype=torch.int32, device=DEV)
     dps = torch.empty((8,), dtype=torch.int32, device=DEV)
-    t.prefetch([2, 9, 14], hb, st, H, D, dsc, dps)
-    t.prefetch([9, 14, 17], hb, st, H, D, dsc, dps)      # prediction for this chunk
+    t.prefetch([2, 9, 14], hb, st, H, D, dsc, dps, copy_mode=copy_mode)
+    t.prefetch([9, 14, 17], hb, st, H, D, dsc, dps, copy_mode=copy_mode)   # this chunk's prediction
     actual = torch.tensor([3, 9, 14], dtype=torch.int32, device=DEV)   # 3 is not staged
-    say("tier_window", int4)
+    say("tier_window", int4, copy_mode)
     slots, miss = w.wkv_tier_resolve(actual, dsc, dps)
     sink = S.segment_kv(2, 1, 32, H, D, device=DEV)
     cur = S.segment_kv(2, 2, 48, H, D, device=DEV)

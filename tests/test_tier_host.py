@@ -22,15 +22,24 @@ def w():
 
 
 @pytest.mark.parametrize("seed,n_slots", [(0, 4), (1, 8), (2, 13), (3, 64), (4, 1)])
-def test_plan_matches_oracle_on_random_streams(w, seed, n_slots):
+@pytest.mark.parametrize("with_keep", [False, True])
+def test_plan_matches_oracle_on_random_streams(w, seed, n_slots, with_keep):
     rng = np.random.default_rng(seed)
     t = w.Tier(n_slots)
     sc, lu, clk = [-1] * n_slots, [0] * n_slots, 0
     for step in range(300):
         n = int(rng.integers(1, n_slots + 1))
         ids = [int(x) for x in rng.choice(3 * n_slots + 5, size=n, replace=False)]
-        so, cp = t.plan(ids)
-        sc, lu, clk, oso, ocp = O.tier_plan(sc, lu, clk, ids)
+        keep = [int(x) for x in rng.choice(3 * n_slots + 5, size=int(rng.integers(0, n_slots)),
+                                           replace=False)] if with_keep else []
+        r = O.tier_plan(sc, lu, clk, ids, tuple(keep))
+        if r is None:
+            with pytest.raises(w.WkvError):
+                t.plan(ids, keep)
+            assert t.slot_chunk == sc          # a refused request changes nothing
+            continue
+        so, cp = t.plan(ids, keep)
+        sc, lu, clk, oso, ocp = r
         assert so == oso and cp == ocp, step
         assert t.slot_chunk == sc
         assert [int(t.t.last_use[i]) for i in range(n_slots)] == lu and int(t.t.clock) == clk
@@ -60,12 +69,18 @@ def test_prefetch_and_resolve_validation(w):
     ids = (C.c_int32 * 2)(1, 2)
     nc = C.c_int32(0)
     f = w._tier_prefetch
-    assert f(None, C.cast(ids, C.c_void_p), 2, C.byref(hb), C.byref(sb), 2, 64, A, A, C.byref(nc), None) == 1
+
+    def call(t_, ids_, hb_, sb_, D=64, mode=0):
+        return f(t_, C.cast(ids_, C.c_void_p), 2, None, 0, hb_, sb_, 2, D, mode, A, A,
+                 C.byref(nc), None)
+
+    assert call(None, ids, C.byref(hb), C.byref(sb)) == 1
     bad = w.wkv_bank(0, 5, 8, A, A, None, None)          # staging M != n_slots
-    assert f(C.byref(tt), C.cast(ids, C.c_void_p), 2, C.byref(hb), C.byref(bad), 2, 64, A, A, C.byref(nc), None) == 2
+    assert call(C.byref(tt), ids, C.byref(hb), C.byref(bad)) == 2
     big = (C.c_int32 * 2)(1, 10)                         # id >= host M
-    assert f(C.byref(tt), C.cast(big, C.c_void_p), 2, C.byref(hb), C.byref(sb), 2, 64, A, A, C.byref(nc), None) == 2
-    assert f(C.byref(tt), C.cast(ids, C.c_void_p), 2, C.byref(hb), C.byref(sb), 2, 96, A, A, C.byref(nc), None) == 7
+    assert call(C.byref(tt), big, C.byref(hb), C.byref(sb)) == 2
+    assert call(C.byref(tt), ids, C.byref(hb), C.byref(sb), D=96) == 7
+    assert call(C.byref(tt), ids, C.byref(hb), C.byref(sb), mode=5) == 7
     assert [tt.chunk[i] for i in range(4)] == [-1] * 4   # failed calls leave the table alone
     r = w._tier_resolve
     assert r(None, 2, A, 4, A, A, None, None) == 1
