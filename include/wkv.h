@@ -6,11 +6,13 @@
  *   [WorldKV]   "WorldKV: Efficient World Memory with World Retrieval and
  *               Compression": Sec. 4.2 World Retrieval, Sec. 4.3 World
  *               Compression, Sec. 5.1 Implementation Details.
- *   [WorldPager] WorldPager summary: abstract and Fig. 2 (int4 KV store,
- *               retrieval from the extrapolated camera pose).
+ *   [WorldPager] WorldPager summary: abstract and Fig. 2 (int4 KV store in
+ *               pinned host memory, retrieval from the extrapolated camera
+ *               pose, no stall on a miss).
  *   [WorldAttention] WorldAttention breakdown: scaled dot-product attention of
  *               the current chunk over visible keys; the index-mapping and
- *               contiguous-copy stages of its kernel section.
+ *               contiguous-copy stages of its kernel section; page scores as
+ *               the dot product of the mean query and the mean key.
  *
  * Conventions for every call:
  *   - bf16 tensors are passed as uint16_t bit patterns. K / V / Q tensors are
@@ -23,9 +25,12 @@
  *     "enqueued". A device-side fault surfaces at the caller's next
  *     synchronisation, as with any HIP launch.
  *   - All argument checks run on the host before anything is enqueued. A
- *     non-OK status enqueues nothing and leaves every output untouched; the
- *     reason is available from wkv_last_error() (thread-local text).
- *   - Calls are stateless and reentrant; ordering is the stream's.
+ *     non-OK status from a check enqueues nothing and leaves every output
+ *     untouched; the reason is available from wkv_last_error() (thread-local
+ *     text). WKV_ERR_HIP reports a runtime failure of an enqueue, after which
+ *     the call's earlier work may already be enqueued.
+ *   - Calls are stateless and reentrant; ordering is the stream's. The host
+ *     tier's slot table is state the caller owns and passes in.
  *   - Supported shapes: D in {64, 128}; H >= 1; H*D <= 8192.
  */
 #ifndef WKV_H_
