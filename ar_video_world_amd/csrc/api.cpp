@@ -72,6 +72,9 @@ int64_t keep_count(int32_t F, int32_t T, float r) {
   return n;
 }
 
+// Largest grid y / z extent: the batch and row-slice counts ride on those axes.
+constexpr int kMaxGridYZ = 65535;
+
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
@@ -99,8 +102,9 @@ wkv_status compress_common(const char* fn, const uint16_t* k, const uint16_t* v,
   if (!k || !v || !kept_idx)
     return fail(WKV_ERR_NULL, "%s: k, v and kept_idx are required", fn);
   if (wkv_status st = check_hd(H, D)) return st;
-  if (B < 1 || F < 2 || F > 4 || T < 1)
-    return fail(WKV_ERR_SHAPE, "%s: need B>=1, 2<=F<=4, T>=1 (B=%d F=%d T=%d)", fn, B, F, T);
+  if (B < 1 || B > kMaxGridYZ || F < 2 || F > 4 || T < 1)
+    return fail(WKV_ERR_SHAPE, "%s: need 1<=B<=%d, 2<=F<=4, T>=1 (B=%d F=%d T=%d)", fn,
+                kMaxGridYZ, B, F, T);
   if ((int64_t)(F - 1) * T > 8192)
     return fail(WKV_ERR_SHAPE, "%s: (F-1)*T=%lld exceeds 8192", fn, (long long)(F - 1) * T);
   if ((int64_t)B * F * T * H * D >= ((int64_t)1 << 40))
@@ -192,8 +196,10 @@ wkv_status wkv_mean_rows(const uint16_t* x, int32_t B, int32_t L_in, const int32
                          size_t ws_bytes, wkv_stream_t stream) {
   if (!x || !out || !ws) return fail(WKV_ERR_NULL, "wkv_mean_rows: x, out and ws are required");
   if (wkv_status st = check_hd(H, D)) return st;
-  if (B < 1 || L < 1 || L_in < 1 || (!rows && L > L_in))
-    return fail(WKV_ERR_SHAPE, "wkv_mean_rows: B=%d L_in=%d L=%d", B, L_in, L);
+  if (B < 1 || B > kMaxGridYZ || L < 1 || L_in < 1 || (!rows && L > L_in) ||
+      wkv::mean_rows_slices(L) > kMaxGridYZ)
+    return fail(WKV_ERR_SHAPE, "wkv_mean_rows: B=%d L_in=%d L=%d (B <= %d, L <= %d)", B, L_in, L,
+                kMaxGridYZ, kMaxGridYZ * 64);
   if ((int64_t)B * L_in * H * D >= ((int64_t)1 << 40) || (int64_t)B * L >= ((int64_t)1 << 31))
     return fail(WKV_ERR_SHAPE, "wkv_mean_rows: input too large");
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (rows && !aligned16(rows)))

@@ -151,7 +151,7 @@ size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H,
  *   scores     double [B][(F-1)*T] or NULL    optional output
  *   ws         >= wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
  *              bytes (may be NULL when that is 0)
- * Limits: 1 <= B; 2 <= F <= 4; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1.
+ * Limits: 1 <= B <= 65535; 2 <= F <= 4; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1.
  * Errors: WKV_ERR_UNSUPPORTED for an unknown score_mode. */
 wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
                               int32_t F, int32_t T, int32_t H, int32_t D,
@@ -258,8 +258,8 @@ size_t wkv_mean_rows_workspace_bytes(int32_t B, int32_t L, int32_t H, int32_t D)
  *                                               outside [0, L_in) adds zeros
  *   out    double [B][H][D]                     output
  *   ws     >= wkv_mean_rows_workspace_bytes(B, L, H, D) bytes
- * Limits: B >= 1; 1 <= L; L <= L_in when rows is NULL; H*D <= 8192, D in
- * {64, 128}. Bitwise reproducible (fixed summation order). */
+ * Limits: 1 <= B <= 65535; 1 <= L <= 4194240; L <= L_in when rows is NULL;
+ * H*D <= 8192, D in {64, 128}. Bitwise reproducible (fixed summation order). */
 wkv_status wkv_mean_rows(const uint16_t* x, int32_t B, int32_t L_in, const int32_t* rows,
                          int32_t L, int32_t H, int32_t D, double* out, void* ws,
                          size_t ws_bytes, wkv_stream_t stream);

@@ -92,6 +92,7 @@ def test_compress_validation(w):
     assert call(F=5) == 2
     assert call(T=0) == 2
     assert call(T=8193, F=2) == 2
+    assert call(B=65536) == 2         # the batch rides on a grid axis of at most 65535
     assert call(r=1.5) == 3
     assert call(r=-0.1) == 3
     assert call(r=float("nan")) == 3
@@ -204,6 +205,8 @@ def test_query_retrieval_validation(w):
     assert call(D=32) == 7
     assert call(L=101) == 2                 # more rows than the input holds
     assert call(L=0) == 2
+    assert call(B=65536, Lin=1, L=1) == 2
+    assert call(rows=A, Lin=1, L=65535 * 64 + 1) == 2   # row slices ride on a grid axis
     assert call(out=MIS) == 5
     assert call(wsb=100) == 6
     q = w._query_topk
