@@ -291,18 +291,20 @@ wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32
     for (int j = 0; j < i; ++j)
       if (ids[j] == ids[i]) return fail(WKV_ERR_SHAPE, "wkv_tier_plan: id %d repeated", ids[i]);
   }
-  // Work on a copy: a request that does not fit leaves the table unchanged.
+  // Work on copies: a request that does not fit leaves the table and every
+  // output unchanged.
   wkv_tier nt = *t;
+  int32_t so[WKV_TIER_MAX_SLOTS], ci[WKV_TIER_MAX_SLOTS], cs[WKV_TIER_MAX_SLOTS];
   const uint64_t stamp = ++nt.clock;
   bool taken[WKV_TIER_MAX_SLOTS] = {};
   for (int s = 0; s < nt.n_slots; ++s)
     for (int j = 0; j < n_keep && !taken[s]; ++j)
       taken[s] = nt.chunk[s] >= 0 && nt.chunk[s] == keep_ids[j];
   for (int i = 0; i < n; ++i) {
-    slot_of[i] = -1;
+    so[i] = -1;
     for (int s = 0; s < nt.n_slots; ++s)
       if (nt.chunk[s] == ids[i]) {
-        slot_of[i] = s;
+        so[i] = s;
         taken[s] = true;
         nt.last_use[s] = stamp;
         break;
@@ -310,7 +312,7 @@ wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32
   }
   int nc = 0;
   for (int i = 0; i < n; ++i) {
-    if (slot_of[i] >= 0) continue;
+    if (so[i] >= 0) continue;
     int v = -1;
     for (int s = 0; s < nt.n_slots; ++s)
       if (!taken[s] && (v < 0 || nt.last_use[s] < nt.last_use[v])) v = s;  // ties: lower slot
@@ -320,12 +322,15 @@ wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32
     nt.chunk[v] = ids[i];
     nt.last_use[v] = stamp;
     taken[v] = true;
-    slot_of[i] = v;
-    copy_ids[nc] = ids[i];
-    copy_slots[nc] = v;
+    so[i] = v;
+    ci[nc] = ids[i];
+    cs[nc] = v;
     ++nc;
   }
   *t = nt;
+  std::copy(so, so + n, slot_of);
+  std::copy(ci, ci + nc, copy_ids);
+  std::copy(cs, cs + nc, copy_slots);
   *n_copies = nc;
   return WKV_OK;
 }

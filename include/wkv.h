@@ -307,7 +307,8 @@ wkv_status wkv_tier_init(wkv_tier* t, int32_t n_slots);
  * whose slots must not be evicted, because an enqueued chunk still reads
  * them. Writes slot_of[n], and the chunks to copy as copy_ids / copy_slots
  * [*n_copies] (host arrays of n entries). Updates t; a request that cannot
- * fit beside the kept chunks is WKV_ERR_SHAPE and changes nothing. */
+ * fit beside the kept chunks is WKV_ERR_SHAPE and changes neither t nor any
+ * output. */
 wkv_status wkv_tier_plan(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
                          int32_t n_keep, int32_t* slot_of, int32_t* copy_ids,
                          int32_t* copy_slots, int32_t* n_copies);

@@ -131,3 +131,18 @@ def test_pose_extrapolate_equals_oracle(w):
         last[3] = np.float32(rng.uniform(-np.pi, np.pi))
         got = np.array(w.wkv_pose_extrapolate(prev, last), dtype=np.float32)
         assert np.array_equal(got, O.pose_extrapolate(prev, last))
+
+
+def test_refused_plan_leaves_outputs_untouched(w):
+    t = w.Tier(2)
+    t.plan([5, 6])
+    ids = (C.c_int32 * 2)(7, 8)
+    keep = (C.c_int32 * 1)(5)                 # slot of 5 is kept: 2 new ids cannot fit
+    so = (C.c_int32 * 2)(-77, -77)
+    ci = (C.c_int32 * 2)(-77, -77)
+    cs = (C.c_int32 * 2)(-77, -77)
+    nc = C.c_int32(-77)
+    assert w._tier_plan(C.byref(t.t), ids, 2, keep, 1, so, ci, cs, C.byref(nc)) == 2
+    assert list(so) == [-77, -77] and list(ci) == [-77, -77] and list(cs) == [-77, -77]
+    assert nc.value == -77
+    assert t.slot_chunk == [5, 6]
