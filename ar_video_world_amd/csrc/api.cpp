@@ -362,6 +362,16 @@ wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const i
   int32_t slot_of[WKV_TIER_MAX_SLOTS], cid[WKV_TIER_MAX_SLOTS], cslot[WKV_TIER_MAX_SLOTS], nc = 0;
   if (wkv_status st = wkv_tier_plan(&nt, ids, n, keep_ids, n_keep, slot_of, cid, cslot, &nc))
     return st;
+  // A copy that was enqueued may already be overwriting its slot: if a later
+  // step fails, those slots are marked empty in the caller's table so that no
+  // later request trusts their contents.
+  auto abandon = [&](hipError_t e, const char* what) {
+    for (int i = 0; i < nc; ++i) {
+      t->chunk[cslot[i]] = -1;
+      t->last_use[cslot[i]] = 0;
+    }
+    return hip_fail(e, what);
+  };
   const size_t rows = (size_t)host_bank->Lc * H * D;
   const size_t kv_bytes = q4 ? rows / 2 : rows * 2;
   const size_t sc_bytes = q4 ? rows / 32 * 2 : 0;
@@ -376,7 +386,7 @@ wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const i
         hipError_t e = hipMemcpyAsync(static_cast<char*>(const_cast<void*>(to[c])) + dst * bytes,
                                       static_cast<const char*>(from[c]) + src * bytes, bytes,
                                       hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch copy");
+        if (e != hipSuccess) return abandon(e, "wkv_tier_prefetch copy");
       }
     }
   } else if (nc > 0) {
@@ -406,7 +416,7 @@ wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const i
       c.slot[i] = cslot[i];
     }
     hipError_t e = wkv::tier_copy_launch(c, s);
-    if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch copy");
+    if (e != hipSuccess) return abandon(e, "wkv_tier_prefetch copy");
   }
   wkv::TierTable tt;
   std::memset(&tt, 0, sizeof(tt));
@@ -415,7 +425,7 @@ wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const i
   for (int i = 0; i < nt.n_slots; ++i) tt.chunk[i] = nt.chunk[i];
   for (int i = 0; i < n; ++i) tt.pred[i] = slot_of[i];
   hipError_t e = wkv::tier_table_launch(tt, dev_slot_chunk, dev_pred_slot, s);
-  if (e != hipSuccess) return hip_fail(e, "wkv_tier_prefetch table");
+  if (e != hipSuccess) return abandon(e, "wkv_tier_prefetch table");
   *t = nt;
   *n_copies = nc;
   return WKV_OK;

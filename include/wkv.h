@@ -333,7 +333,8 @@ enum { WKV_TIER_COPY_KERNEL = 0, WKV_TIER_COPY_ENGINE = 1 };
  * (device; values captured at enqueue). The caller orders `stream` after
  * the last reader of the staging bank and its readers after this call's
  * work (events). *n_copies (host) receives the number of chunks copied.
- * staging->M must equal t->n_slots. */
+ * staging->M must equal t->n_slots. On WKV_ERR_HIP the slots this request
+ * was filling are marked empty in t (their contents are not to be trusted). */
 wkv_status wkv_tier_prefetch(wkv_tier* t, const int32_t* ids, int32_t n, const int32_t* keep_ids,
                              int32_t n_keep, const wkv_bank* host_bank, const wkv_bank* staging,
                              int32_t H, int32_t D, int32_t copy_mode, int32_t* dev_slot_chunk,
