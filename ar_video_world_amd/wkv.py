@@ -434,9 +434,11 @@ def _pose_tuple(p) -> wkv_pose:
 
 
 def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
-                  want_dist: bool = True, want_query: bool = False, stream=None):
+                  want_dist: bool = True, want_query: bool = False, stream=None,
+                  out_idx: Optional[torch.Tensor] = None):
     """Top-k stored chunks by camera-pose distance. bank_poses: float32 [M, 4]
     on the device. query_hist: one pose (x, y, z, yaw) or [prev, last].
+    out_idx: optional int32 device tensor of >= k_eff elements to write into.
     Returns (idx int32 [k_eff], dist float64 [k_eff] or None, query or None)."""
     if bank_poses.dtype != torch.float32 or bank_poses.dim() != 2 or bank_poses.shape[1] != 4:
         raise TypeError("bank_poses: expected float32 [M, 4]")
@@ -449,7 +451,14 @@ def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
     arr = (wkv_pose * max(n_hist, 1))(*[_pose_tuple(p) for p in hist])
     k_eff = min(int(k), M) if k >= 1 else 1
     dev = bank_poses.device
-    idx = torch.empty(max(k_eff, 1), dtype=torch.int32, device=dev)
+    if out_idx is None:
+        idx = torch.empty(max(k_eff, 1), dtype=torch.int32, device=dev)
+    else:
+        if (out_idx.dtype != torch.int32 or not out_idx.is_contiguous()
+                or out_idx.numel() < k_eff or out_idx.device != dev):
+            raise TypeError("out_idx: expected a contiguous int32 tensor of >= k_eff elements "
+                            "on the bank's device")
+        idx = out_idx[:k_eff]
     dist = torch.empty(max(k_eff, 1), dtype=torch.float64, device=dev) if want_dist else None
     q = torch.empty(4, dtype=torch.float32, device=dev) if want_query else None
     st = _pose_topk(_ptr(bank_poses), M, arr, n_hist, int(k), _ptr(idx), _ptr(dist),
