@@ -25,10 +25,14 @@
 //   * Softmax in base 2 with a fixed per-row reference: p = exp2(s*c - mref),
 //     c = scale*log2(e), converted to bf16, and the row sum is a bf16 dot2 of
 //     exactly the weights the P*V product uses. There is no per-tile row max:
-//     a range guard on the tile's row sums (rare branch) moves mref to the
-//     row max only when some weight would approach the fp32/bf16 range or a
-//     row has not accumulated any weight yet. O and l always share mref, so
-//     the result does not depend on where it sits.
+//     the first tile of a block's key range sets mref to that tile's row max
+//     (so the row sum is >= 1 from then on and cannot underflow), and after
+//     that a range guard on the tile's row sums (rare branch) moves mref up
+//     only when some weight would approach the fp32/bf16 range. O and l
+//     always share mref, so the result does not depend on where it sits.
+//   * While a wave issues its P*V MFMAs it runs at raised priority, so when
+//     the two waves sharing a SIMD are in different phases the MFMA-dense one
+//     issues first and the other's softmax VALU fills the gaps.
 //   * The S^T product of tile t+1 is issued ahead of the softmax of tile t,
 //     so one wave has MFMA work independent of its VALU work.
 //   * Long key ranges with few query tiles are split over blocks; each split
@@ -54,7 +58,6 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kBigSum = 1073741824.0f;     // 2^30: largest accepted tile row sum
-constexpr float kTinySum = 8.673617e-19f;    // 2^-60: smallest accepted running row sum
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -321,15 +324,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
+    // First tile of the range: the reference becomes the tile's row max, so
+    // the row's largest weight so far is 1 and its sum stays >= 1 (nothing
+    // that dominates the row can underflow). Uniform branch, once per block.
+    if (it == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kt][e]);
+      mx = max_halves(mx) * c;
+      if (mx > -INFINITY) {
+        mref = mx;
+        weights();
+      }
+    }
     // Range guard. The reference mref stays where it is while every half-row
-    // tile sum is <= 2^30 (no weight near the fp32/bf16 range) and every row
-    // has accumulated >= 2^-60 (what dominates it has not underflowed).
-    // Otherwise the row's reference moves to its max (up only, once weight
-    // has accumulated; O and l are rescaled by the same factor, or reset if
-    // nothing has accumulated) and the weights are recomputed. O and l always
-    // share mref, so the result is the same for any reference. Both halves
-    // of a row decide on row-wide quantities, so they always agree.
-    if (__any(!(ts <= kBigSum) || !(sum_halves(lsum + ts) >= kTinySum))) {
+    // tile sum is <= 2^30 (no weight near the fp32/bf16 range). Otherwise the
+    // row's reference moves to its max (up only, once weight has accumulated;
+    // O and l are rescaled by the same factor, or reset if nothing has
+    // accumulated) and the weights are recomputed. O and l always share mref,
+    // so the result is the same for any reference. Both halves of a row
+    // decide on row-wide quantities, so they always agree.
+    if (__any(!(ts <= kBigSum))) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -350,6 +367,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     lsum += ts;
 
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -370,6 +388,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     sc[0] = sn[0];
     sc[1] = sn[1];
+    __builtin_amdgcn_s_setprio(0);
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(t+2), V(t+1) have landed
     __syncthreads();
