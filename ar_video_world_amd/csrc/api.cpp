@@ -517,6 +517,9 @@ wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,
   if (p.Nk > win_rows)
     return fail(WKV_ERR_SHAPE, "wkv_assemble_window: window needs %lld rows, capacity %lld",
                 (long long)p.Nk, (long long)win_rows);
+  if (p.Nk > wkv::kMaxWindowRows)
+    return fail(WKV_ERR_SHAPE, "wkv_assemble_window: window of %lld rows exceeds %lld",
+                (long long)p.Nk, (long long)wkv::kMaxWindowRows);
   if (p.Nk == 0) return WKV_OK;
   p.bank_k = n_ret ? bank->k : nullptr;
   p.bank_v = n_ret ? bank->v : nullptr;

@@ -9,6 +9,7 @@
 namespace wkv {
 
 constexpr int kMaxSegments = 16;  // sink + up to 14 recent + current
+constexpr int64_t kMaxWindowRows = (1LL << 26) - 1;  // one 64-lane block per row, < 2^32 lanes
 
 // ---- compression
 int compress_score_tile(int B, int T, int H);

@@ -364,7 +364,9 @@ wkv_status wkv_tier_resolve(const int32_t* actual_idx, int32_t n, const int32_t*
  *                                            dequantised on the fly)
  *   then recent[0], ..., recent[n_recent-1], then current,
  * Nk = n_s + n_ret*Lc + sum(recent[].n) + current.n, which must not exceed
- * win_rows. A retrieved id outside [0, M) yields zero rows (no fault).
+ * win_rows nor 2^26 - 1 (one 64-lane wave copies each row and a launch holds
+ * fewer than 2^32 lanes): WKV_ERR_SHAPE otherwise. A retrieved id outside
+ * [0, M) yields zero rows (no fault).
  *   sink, current  [host] wkv_segment
  *   bank           [host] wkv_bank (device arrays inside)
  *   retrieved_idx  int32 [n_ret] device (e.g. out_idx of wkv_pose_topk)
