@@ -229,3 +229,17 @@ def test_pose_so3_validation(w):
     assert f(A, 4, q, 0, A, None, None) == 4
     assert f(MIS, 4, q, 2, A, None, None) == 5
     assert C.sizeof(w.wkv_pose_q) == 32
+
+
+def test_assemble_window_row_cap(w):
+    """A window row is one 64-lane block and a launch holds fewer than 2^32
+    lanes: windows past 2^26 - 1 rows are refused before any launch."""
+    f = w._assemble
+    R = C.byref
+    big = w.wkv_segment(A, A, 1 << 25)
+    bank = w.wkv_bank(0, 4, 8, A, A, None, None)
+    rec = (w.wkv_segment * 1)(big)
+    cur = w.wkv_segment(A, A, 0)
+    # 2^25 + 2^25 rows = 2^26 > 2^26 - 1
+    assert f(R(big), R(bank), A, 0, rec, 1, R(cur), 2, 64, A, A, 1 << 27, None) == 2
+    assert "exceeds" in w.wkv_last_error()
