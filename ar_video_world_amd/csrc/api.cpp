@@ -124,7 +124,8 @@ wkv_status compress_common(const char* fn, const uint16_t* k, const uint16_t* v,
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(WKV_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn,
                 ws ? ws_bytes : (size_t)0, L.total);
-  if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean) > (size_t)max_lds_per_block())
+  if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean, dst.k_packed != nullptr) >
+                   (size_t)max_lds_per_block())
     return fail(WKV_ERR_SHAPE, "%s: H*D too large for the score kernel's LDS", fn);
   char* wsb = static_cast<char*>(ws);
   double* sbuf = scores ? scores : (score ? reinterpret_cast<double*>(wsb + L.scores) : nullptr);

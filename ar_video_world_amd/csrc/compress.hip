@@ -535,11 +535,16 @@ void launch_anchor_mean(const uint16_t* k, int B, int F, int T, int H, double* p
 
 }  // namespace
 
-// Tokens per score block: at least one full pass of (token, head) pairs, and
-// grown while the grid still has >= 2048 blocks.
-int compress_score_tile(int B, int T, int H) {
+// Tokens per score block: one full pass of (token, head) pairs. The tile
+// grows while the grid still has >= 2048 blocks when each block has fixed
+// work to spread over more tokens: encoding the anchor rows to int4, or
+// staging the anchor mean in LDS. On 300 units of 3 x 880 x 12 x 128 growth
+// took the int4 batch from 0.45 to 0.49 of HBM peak and the anchor-mean batch
+// from 0.58 to 0.64, while the position-mode bf16 batch ran 1-4 % faster on
+// the smallest tile.
+int compress_score_tile(int B, int T, int H, bool grow) {
   int tt = (kPairsPerPass + H - 1) / H;
-  while (tt * 2 <= 64 && tt * 2 * H <= 512 &&
+  while (grow && tt * 2 <= 64 && tt * 2 * H <= 512 &&
          (long long)((T + tt * 2 - 1) / (tt * 2)) * B >= 2048)
     tt *= 2;
   return tt < T ? tt : T;
@@ -547,8 +552,8 @@ int compress_score_tile(int B, int T, int H) {
 
 int compress_mean_slices(int T) { return (T + kMeanTok - 1) / kMeanTok; }
 
-size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean) {
-  const int TT = compress_score_tile(B, T, H);
+size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4) {
+  const int TT = compress_score_tile(B, T, H, q4 || mean);
   return ((size_t)TT * (F - 1) * H + (mean ? (size_t)H * (D + kAbarSkew) : 0)) * sizeof(double);
 }
 
@@ -575,7 +580,7 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                          mean_part, ns, T, H, abar);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int TT = compress_score_tile(B, T, H);
+    const int TT = compress_score_tile(B, T, H, q4 || abar != nullptr);
     e = (D == 128) ? dispatch_score_F<128>(k, B, F, T, H, TT, scores, out, q4, Lc, abar, s)
                    : dispatch_score_F<64>(k, B, F, T, H, TT, scores, out, q4, Lc, abar, s);
     if (e != hipSuccess) return e;

@@ -12,9 +12,9 @@ constexpr int kMaxSegments = 16;  // sink + up to 14 recent + current
 constexpr int64_t kMaxWindowRows = (1LL << 26) - 1;  // one 64-lane block per row, < 2^32 lanes
 
 // ---- compression
-int compress_score_tile(int B, int T, int H);
+int compress_score_tile(int B, int T, int H, bool grow);
 int compress_mean_slices(int T);  // anchor-token slices of the anchor-mean sums
-size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean);
+size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4);
 // Destination of the compressed rows: bf16 rows (k, v) when k_packed is
 // null, else int4 codes (k_packed, v_packed: [B][Lc][H][D/2]) with bf16 group
 // scales (k_scale, v_scale: [B][Lc][H][D/32]).
