@@ -91,29 +91,36 @@ __device__ __forceinline__ uint32_t int4_encode_quad(const uint4& x, uint16_t* s
   float m = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  m = fmaxf(m, __shfl_xor(m, 2, 64));
-  const uint16_t sb = f32_to_bf16(__fdiv_rn(m, 7.0f));
+  // Max over the quad with two row permutes (DPP quad_perm [1,0,3,2], then
+  // [2,3,0,1]): lanes l^1, then l^2.
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+  // m / 7 correctly rounded, as one Newton step from m * RN(1/7): the residual
+  // m - 7*y0 is exact, and the corrected quotient equals the correctly
+  // rounded one for every bf16 m, subnormals included (checked exhaustively).
+  constexpr float kInv7 = 1.0f / 7.0f;  // RN(1/7)
+  const float y0 = m * kInv7;
+  const float m7 = __builtin_isinf(m) ? m : fmaf(fmaf(-y0, 7.0f, m), kInv7, y0);
+  const uint16_t sb = f32_to_bf16(m7);
   const float sc = bf16_to_f32(sb);
   uint32_t out = 0;
   if (sc != 0.f) {
-    // x and sc carry 8-bit significands, so an exact quotient x / sc that is
-    // not a half-integer lies at least 1/1020 from one: the correctly
-    // rounded float32 quotient and x * rcp(sc) (error < 2e-6 for |x/sc| <= 8)
-    // round to the same integer. Exact half-integers are told apart by the
-    // exact residual x - q*sc (q has 4 bits, so the fma is exact) and moved
-    // to the even neighbour. A scale so small that rcp overflows takes the
-    // division.
-    const float inv = __builtin_amdgcn_rcpf(sc);
+    // inv is the correctly rounded 1/sc. k = rint(x * inv) is the nearest
+    // integer to x / sc except at exact half-integers: x and sc carry 8-bit
+    // significands, so any other quotient lies at least 1/1020 from a
+    // half-integer, far beyond the error of x * inv. The residual
+    // r = x - k*sc is exact (k has 4 bits), and k + r*inv lands exactly on
+    // the half-integer at a tie and within 0.499 of k otherwise, so its rint
+    // is the round-half-even quotient in every case (checked exhaustively
+    // against exact rounding for all bf16 pairs with |x / sc| <= 7.02). A
+    // scale so small that 1/sc overflows, or infinite, takes the division.
+    const float inv = __fdiv_rn(1.0f, sc);
     float q[8];
-    if (inv < 3.0e38f) {
-      const float hs = 0.5f * sc;
+    if (inv < 3.0e38f && inv > 0.f) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float qa = rintf(v[e] * inv);
-        const float r = fmaf(-qa, sc, v[e]);
-        const bool tie_odd = (fabsf(r) == hs) & (((int)qa & 1) != 0);
-        q[e] = tie_odd ? qa + copysignf(1.f, r) : qa;
+        const float k = rintf(v[e] * inv);
+        q[e] = rintf(fmaf(fmaf(-k, sc, v[e]), inv, k));
       }
     } else {
 #pragma unroll
