@@ -114,21 +114,24 @@ __device__ __forceinline__ uint32_t int4_encode_quad(const uint4& x, uint16_t* s
     // is the round-half-even quotient in every case (checked exhaustively
     // against exact rounding for all bf16 pairs with |x / sc| <= 7.02). A
     // scale so small that 1/sc overflows, or infinite, takes the division.
+    // For finite groups |x / sc| <= 7 / (1 - 2^-9) < 7.5, so every code is in
+    // [-7, 7]. Adding 1.5 * 2^23 rounds k + r*inv half-to-even to an integer
+    // and leaves it, in two's complement, in the low mantissa bits.
     const float inv = __fdiv_rn(1.0f, sc);
-    float q[8];
     if (inv < 3.0e38f && inv > 0.f) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float k = rintf(v[e] * inv);
-        q[e] = rintf(fmaf(fmaf(-k, sc, v[e]), inv, k));
+        const float t = fmaf(fmaf(-k, sc, v[e]), inv, k) + 12582912.0f;
+        out |= (__float_as_uint(t) & 0xFu) << (4 * e);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = rintf(__fdiv_rn(v[e], sc));
+      for (int e = 0; e < 8; ++e) {
+        const float q = rintf(__fdiv_rn(v[e], sc));
+        out |= ((uint32_t)(int)fminf(fmaxf(q, -8.f), 7.f) & 0xFu) << (4 * e);
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      out |= ((uint32_t)(int)fminf(fmaxf(q[e], -8.f), 7.f) & 0xFu) << (4 * e);
   }
   *sbits = sb;
   return out;

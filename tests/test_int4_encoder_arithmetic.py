@@ -5,8 +5,9 @@ definitions:
 
 * RN32(m / 7) == fma(fma(-y0, 7, m), RN32(1/7), y0) with y0 = RN32(m * RN32(1/7)),
   for every positive finite bf16 m (subnormals included);
-* rint(fma(fma(-k, s, x), inv, k)) with k = rint(RN32(x * inv)) and
-  inv = RN32(1 / s) is the round-half-even integer of the exact x / s, for
+* the low nibble of RN32(fma(fma(-k, s, x), inv, k) + 1.5 * 2^23), with
+  k = rint(RN32(x * inv)) and inv = RN32(1 / s), is the round-half-even
+  integer of the exact x / s in two's complement, for
   every bf16 x and bf16 scale s with |x / s| <= 7.02 (the largest quotient
   an encoded group can hold is 7 / (1 - 2^-9)).
 
@@ -70,7 +71,10 @@ def _check_codes(sbits):
     S, X, inv = S[ok], X[ok], inv[ok]
     k = np.rint((X * inv).astype(F32))
     r = (X.astype(F64) - k.astype(F64) * S.astype(F64)).astype(F32)
-    q = np.rint((r.astype(F64) * inv.astype(F64) + k.astype(F64)).astype(F32)).astype(np.int64)
+    y = (r.astype(F64) * inv.astype(F64) + k.astype(F64)).astype(F32)
+    t = (y + F32(12582912.0)).astype(F32)          # the kernel's rounding add
+    nib = (t.view(np.uint32) & 0xF).astype(np.int64)
+    q = np.where(nib >= 8, nib - 16, nib)          # two's complement of the low nibble
     want = _rne_quotient(X, S)
     bad = np.nonzero(q != want)[0]
     assert bad.size == 0, (X[bad[:5]], S[bad[:5]], q[bad[:5]], want[bad[:5]])
