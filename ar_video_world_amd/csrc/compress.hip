@@ -545,15 +545,17 @@ void launch_anchor_mean(const uint16_t* k, int B, int F, int T, int H, double* p
 
 }  // namespace
 
-// Tokens per score block: one full pass of (token, head) pairs. The tile
-// grows while the grid still has >= 2048 blocks when each block has fixed
-// work to spread over more tokens: encoding the anchor rows to int4, or
-// staging the anchor mean in LDS. On 300 units of 3 x 880 x 12 x 128 growth
-// took the int4 batch from 0.45 to 0.49 of HBM peak and the anchor-mean batch
-// from 0.58 to 0.64, while the position-mode bf16 batch ran 1-4 % faster on
-// the smallest tile.
+// Tokens per score block: as many as one pass of (token, head) pairs holds
+// (5 at 12 heads: one unit of 880 tokens spreads over 176 blocks, each done
+// in one round of loads). When each block has fixed work to spread over more
+// tokens (encoding the anchor rows to int4, or staging the anchor mean in
+// LDS) the tile starts from the smallest that covers a full pass and grows
+// while the grid still has >= 2048 blocks. On 300 units of
+// 3 x 880 x 12 x 128, growth took the int4 batch from 0.45 to 0.49 of HBM
+// peak and the anchor-mean batch from 0.58 to 0.64, while the position-mode
+// bf16 batch ran 1-4 % faster on the smallest tile.
 int compress_score_tile(int B, int T, int H, bool grow) {
-  int tt = (kPairsPerPass + H - 1) / H;
+  int tt = grow ? (kPairsPerPass + H - 1) / H : (H >= kPairsPerPass ? 1 : kPairsPerPass / H);
   while (grow && tt * 2 <= 64 && tt * 2 * H <= 512 &&
          (long long)((T + tt * 2 - 1) / (tt * 2)) * B >= 2048)
     tt *= 2;
