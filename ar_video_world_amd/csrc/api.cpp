@@ -577,6 +577,112 @@ wkv_status wkv_chunk_attention(const uint16_t* q, const uint16_t* k, const uint1
   return WKV_OK;
 }
 
+size_t wkv_attention_window_workspace_bytes(int32_t Nq, int64_t Nk_pad, int32_t H, int32_t D) {
+  if (Nq < 1 || Nk_pad < 1 || Nk_pad >= ((int64_t)1 << 31) || H < 1 || (D != 64 && D != 128))
+    return 0;
+  wkv::AttnPlan p = wkv::attention_plan(Nq, (int)Nk_pad, H, D, num_cus());
+  return wkv::attention_window_table_bytes((int)((Nk_pad + 63) / 64)) +
+         wkv::attention_ws_bytes(p, Nq, H, D);
+}
+
+wkv_status wkv_chunk_attention_window(const uint16_t* q, int32_t Nq, const wkv_segment* sink,
+                                      const wkv_bank* bank, const int32_t* retrieved_idx,
+                                      int32_t n_ret, const wkv_segment* recent, int32_t n_recent,
+                                      const wkv_segment* current, int32_t H, int32_t D,
+                                      float scale, uint16_t* out, float* lse, void* ws,
+                                      size_t ws_bytes, wkv_stream_t stream) {
+  static const char* fn = "wkv_chunk_attention_window";
+  if (!q || !out || !sink || !current)
+    return fail(WKV_ERR_NULL, "%s: q, out, sink and current are required", fn);
+  if (wkv_status st = check_hd(H, D)) return st;
+  if (Nq < 1) return fail(WKV_ERR_SHAPE, "%s: Nq=%d", fn, Nq);
+  if (n_ret < 0 || n_recent < 0 || n_ret + n_recent + 2 > wkv::kMaxWinPieces)
+    return fail(WKV_ERR_SHAPE, "%s: n_ret=%d n_recent=%d (at most %d pieces)", fn, n_ret,
+                n_recent, wkv::kMaxWinPieces);
+  if (n_ret > 0 && (!bank || !retrieved_idx))
+    return fail(WKV_ERR_NULL, "%s: n_ret>0 needs bank and retrieved_idx", fn);
+  if (n_recent > 0 && !recent) return fail(WKV_ERR_NULL, "%s: recent is NULL", fn);
+  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse)) || (ws && !aligned16(ws)) ||
+      (retrieved_idx && !aligned16(retrieved_idx)))
+    return fail(WKV_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+  if ((int64_t)Nq * H * D >= ((int64_t)1 << 31))
+    return fail(WKV_ERR_SHAPE, "%s: Nq*H*D must be < 2^31", fn);
+  if (!(scale == scale) || std::isinf(scale))
+    return fail(WKV_ERR_SHAPE, "%s: scale is not finite", fn);
+  if (n_ret > 0) {
+    if (bank->dtype == WKV_BANK_INT4_G32)
+      return fail(WKV_ERR_UNSUPPORTED, "%s: an int4 bank needs wkv_assemble_window", fn);
+    if (bank->dtype != WKV_BANK_BF16)
+      return fail(WKV_ERR_UNSUPPORTED, "%s: bank dtype %d", fn, bank->dtype);
+    if (bank->M < 1 || bank->Lc < 1)
+      return fail(WKV_ERR_SHAPE, "%s: bank M=%d Lc=%d", fn, bank->M, bank->Lc);
+    if (!bank->k || !bank->v) return fail(WKV_ERR_NULL, "%s: bank k/v NULL", fn);
+    if (!aligned16(bank->k) || !aligned16(bank->v))
+      return fail(WKV_ERR_ALIGN, "%s: bank pointers must be 16-byte aligned", fn);
+  }
+  // Pieces in window order: sink, retrieved slots, recent..., current.
+  wkv::WinPieces w;
+  std::memset(&w, 0, sizeof(w));
+  int np = 0;
+  int64_t tiles = 0;
+  auto add = [&](const uint16_t* k, const uint16_t* v, int32_t n, int32_t slot) -> wkv_status {
+    if (n < 0) return fail(WKV_ERR_SHAPE, "%s: piece %d has n=%d", fn, np, n);
+    if (slot < 0 && n > 0 && (!k || !v))
+      return fail(WKV_ERR_NULL, "%s: piece %d has n=%d but NULL k/v", fn, np, n);
+    if (!aligned16(k) || !aligned16(v))
+      return fail(WKV_ERR_ALIGN, "%s: piece %d pointers must be 16-byte aligned", fn, np);
+    w.k[np] = k;
+    w.v[np] = v;
+    w.n[np] = n;
+    w.slot[np] = slot;
+    w.tile0[np] = (int32_t)tiles;
+    tiles += (n + 63) / 64;
+    ++np;
+    return WKV_OK;
+  };
+  wkv_status st = add(sink->k, sink->v, sink->n, -1);
+  for (int i = 0; st == WKV_OK && i < n_ret; ++i)
+    st = add(static_cast<const uint16_t*>(bank->k), static_cast<const uint16_t*>(bank->v),
+             bank->Lc, i);
+  for (int i = 0; st == WKV_OK && i < n_recent; ++i)
+    st = add(recent[i].k, recent[i].v, recent[i].n, -1);
+  if (st == WKV_OK) st = add(current->k, current->v, current->n, -1);
+  if (st != WKV_OK) return st;
+  const int64_t nk_pad = tiles * 64;
+  if (nk_pad < 1) return fail(WKV_ERR_SHAPE, "%s: the window is empty", fn);
+  if (nk_pad * H * D >= ((int64_t)1 << 31))
+    return fail(WKV_ERR_SHAPE, "%s: padded window of %lld keys: Nk_pad*H*D must be < 2^31", fn,
+                (long long)nk_pad);
+  w.tile0[np] = (int32_t)tiles;
+  w.npieces = np;
+  w.idx = retrieved_idx;
+  w.M = n_ret > 0 ? bank->M : 0;
+  w.Lc = n_ret > 0 ? bank->Lc : 0;
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  const int Nk = (int)nk_pad;
+  const size_t table = wkv::attention_window_table_bytes((int)tiles);
+  if (!ws || ws_bytes < table)
+    return fail(WKV_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu for the tile table", fn,
+                ws ? ws_bytes : (size_t)0, table);
+  const size_t part_bytes = ws_bytes - table;
+  wkv::AttnPlan plan = wkv::attention_plan(Nq, Nk, H, D, num_cus());
+  while (plan.splits > 1 && wkv::attention_ws_bytes(plan, Nq, H, D) > part_bytes) {
+    const int kblocks = Nk / 64;
+    const int want = plan.splits / 2;
+    const int kb_per = (kblocks + want - 1) / want;
+    plan.keys_per_split = kb_per * 64;
+    plan.splits = (kblocks + kb_per - 1) / kb_per;
+  }
+  if (plan.splits <= 1) {
+    plan.splits = 1;
+    plan.keys_per_split = Nk;
+  }
+  hipError_t e = wkv::attention_window_launch(q, w, Nq, H, D, sc, out, lse, plan, ws,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "wkv_chunk_attention_window launch");
+  return WKV_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -41,6 +41,8 @@
 //   * Blocks are renumbered so that each XCD (blocks are dealt round-robin
 //     over the 8 XCDs) works on a contiguous range of (head, split, q-tile):
 //     tiles sharing K/V share that XCD's L2.
+#include <cstring>
+
 #include "wkv_common.hpp"
 #include "wkv_internal.hpp"
 
@@ -137,12 +139,82 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// SEG: the keys are the window's pieces read in place (WinPieces), each
+// padded to whole tiles; Nk is then the padded key count, a multiple of 64.
+// One 64-key tile t of the window read in place, as two 32-byte halves. The
+// first holds what iteration t of the key loop needs in one scalar load: the
+// K rows of tile t+2 and the V rows of tile t+1 (head 0; the loop queues
+// those two loads), how many rows their pieces still have from there (0 for
+// a bank id outside the bank: the tile reads as zero rows), and how many of
+// tile t's 64 keys are real (the rest is padding, masked). The second holds
+// tile t's own rows, for the loads queued before the loop.
+struct __attribute__((aligned(32))) TileEntry {
+  const uint16_t* k_next2;
+  const uint16_t* v_next1;
+  int32_t rows_next2;
+  int32_t rows_next1;
+  int32_t nvalid;
+  int32_t rows;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t pad[2];
+};
+
+// The piece table is the first kernel argument and is read where it lies in
+// the kernel-argument segment; indexing a by-value copy at a run-time index
+// would put it in scratch memory.
+typedef const __attribute__((address_space(4))) WinPieces* kernarg_pieces;
+
+// One thread per tile of the padded key space: resolves the pieces of tiles
+// t, t+1 and t+2 (and their bank ids) once per call.
+__device__ __forceinline__ void resolve_tile(kernarg_pieces win, int64_t HD, int t,
+                                             const uint16_t** k, const uint16_t** v,
+                                             int* rows, int* nvalid) {
+  if (t >= win->tile0[win->npieces]) {
+    *k = nullptr;
+    *v = nullptr;
+    *rows = 0;
+    *nvalid = 0;
+    return;
+  }
+  int pc = 0;
+  while (pc + 1 < win->npieces && t >= win->tile0[pc + 1]) ++pc;
+  const int row0 = (t - win->tile0[pc]) * kBN;
+  int64_t r0 = row0;
+  int n = win->n[pc] - row0;
+  if (win->slot[pc] >= 0) {
+    const int id = win->idx[win->slot[pc]];
+    if (id >= 0 && id < win->M) r0 += (int64_t)id * win->Lc;
+    else n = 0;
+  }
+  *k = win->k[pc] + r0 * HD;
+  *v = win->v[pc] + r0 * HD;
+  *rows = n;
+  *nvalid = min(kBN, win->n[pc] - row0);
+}
+
+__global__ __launch_bounds__(256) void attn_tile_table_kernel(const WinPieces win_arg,
+                                                               int64_t HD,
+                                                               TileEntry* __restrict__ tab) {
+  const kernarg_pieces win = (kernarg_pieces)(__builtin_amdgcn_kernarg_segment_ptr());
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= win->tile0[win->npieces]) return;
+  TileEntry e;
+  const uint16_t* unused;
+  int nv;
+  resolve_tile(win, HD, t, &e.k, &e.v, &e.rows, &e.nvalid);
+  resolve_tile(win, HD, t + 2, &e.k_next2, &unused, &e.rows_next2, &nv);
+  resolve_tile(win, HD, t + 1, &unused, &e.v_next1, &e.rows_next1, &nv);
+  e.pad[0] = e.pad[1] = 0;
+  tab[t] = e;
+}
+
+template <int D, bool SEG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int Nq, int Nk, int H, float c,
     uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ opart,
-    float2* __restrict__ mlpart, int nsplit, int kps) {
+    float2* __restrict__ mlpart, int nsplit, int kps, const TileEntry* __restrict__ tab) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int DT = D / 32;   // d tiles of the PV product
@@ -195,10 +267,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kvo[r] = (uint32_t)((row * (int)HD + (pos ^ kswz<D>(row)) * 8) * 2);
     vvo[r] = (uint32_t)((row * (int)HD + (pos ^ vswz<D>(row)) * 8) * 2);
   }
-  auto issue = [&](const uint16_t* src, int kb, uint8_t* stage, const uint32_t (&vo)[T::LOADS]) {
-    const size_t base = (size_t)kb * HD + (size_t)h * D;
+  // SEG: rows of a tile at `tile` (head 0) with `rows` left in its piece.
+  auto issue_rows = [&](const uint16_t* tile, int rows, uint8_t* stage,
+                        const uint32_t (&vo)[T::LOADS]) {
+    const uint32_t nrec =
+        rows > 0 ? (uint32_t)(((size_t)rows * HD - (size_t)h * D) * 2) : 0u;
+    const rsrc_t rs = make_rsrc(tile + (size_t)h * D, nrec);
+    uint8_t* dst = stage + wave * T::LOADS * 1024;
+#pragma unroll
+    for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rs, dst + r * 1024, vo[r]);
+  };
+  auto issue = [&](bool isv, int kb, uint8_t* stage, const uint32_t (&vo)[T::LOADS]) {
+    const uint16_t* src = (isv ? V : K) + (size_t)kb * HD + (size_t)h * D;
     const uint32_t nrec = (uint32_t)(((size_t)(Nk - kb) * HD - (size_t)h * D) * 2);
-    const rsrc_t rs = make_rsrc(src + base, nrec);
+    const rsrc_t rs = make_rsrc(src, nrec);
     uint8_t* dst = stage + wave * T::LOADS * 1024;
 #pragma unroll
     for (int r = 0; r < T::LOADS; ++r) buffer_load_lds16(rs, dst + r * 1024, vo[r]);
@@ -250,11 +332,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Prologue: K(0), V(0), K(1) in flight, then S^T(0).
   f32x16 sc[2];
-  if (nblk > 0) {
-    issue(K, kbeg, kst0, kvo);
-    issue(V, kbeg, vst0, vvo);
+  if constexpr (!SEG) {
+    if (nblk > 0) {
+      issue(false, kbeg, kst0, kvo);
+      issue(true, kbeg, vst0, vvo);
+    }
+    if (nblk > 1) issue(false, kbeg + kBN, kst1, kvo);
+  } else {
+    if (nblk > 0) {
+      const TileEntry& e0 = tab[kbeg / kBN];
+      issue_rows(e0.k, e0.rows, kst0, kvo);
+      issue_rows(e0.v, e0.rows, vst0, vvo);
+    }
+    if (nblk > 1) {
+      const TileEntry& e1 = tab[kbeg / kBN + 1];
+      issue_rows(e1.k, e1.rows, kst1, kvo);
+    }
   }
-  if (nblk > 1) issue(K, kbeg + kBN, kst1, kvo);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   qk(kst0, sc);
@@ -264,9 +358,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // overlapped with S^T(t+1) from K stage kc; O^T += V(t) P(t) from V stage vc.
   auto tile = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kd, uint8_t* vd) {
     const int kb = kbeg + it * kBN;
-    if (it + 2 < nblk) issue(K, kb + 2 * kBN, kd, kvo);
-    if (it + 1 < nblk) issue(V, kb + kBN, vd, vvo);
+    int nvalid = kBN;
+    if constexpr (!SEG) {
+      if (it + 2 < nblk) issue(false, kb + 2 * kBN, kd, kvo);
+      if (it + 1 < nblk) issue(true, kb + kBN, vd, vvo);
+    } else {
+      // one 32-byte scalar load: this iteration's loads and tile it's keys
+      typedef int i32x8 __attribute__((ext_vector_type(8)));
+      const i32x8 e = *reinterpret_cast<const i32x8*>(tab + kb / kBN);
+      const uint16_t* k2 = reinterpret_cast<const uint16_t*>(
+          (uint64_t)(uint32_t)e[0] | ((uint64_t)(uint32_t)e[1] << 32));
+      const uint16_t* v1 = reinterpret_cast<const uint16_t*>(
+          (uint64_t)(uint32_t)e[2] | ((uint64_t)(uint32_t)e[3] << 32));
+      const int r2 = e[4], r1 = e[5];
+      nvalid = e[6];
+      if (it + 2 < nblk) issue_rows(k2, r2, kd, kvo);
+      if (it + 1 < nblk) issue_rows(v1, r1, vd, vvo);
+    }
 
+    // SEG: mask the padding after the last row of a piece.
+    if constexpr (SEG) {
+      if (nvalid < kBN) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kt * 32 + 16 * (e >> 3) + 8 * g + (e & 7) >= nvalid) sc[kt][e] = -INFINITY;
+      }
+    }
     // Mask keys past the end of this block's range (last tile only).
     if (kb + kBN > kend) {
 #pragma unroll
@@ -463,10 +582,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   if (lse && sub == 0) lse[(size_t)h * Nq + q] = (M + log2f(den)) * kLn2;
 }
 
-template <int D>
+template <int D, bool SEG>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int Nq, int Nk,
                   int H, float scale, uint16_t* out, float* lse, const AttnPlan& plan,
-                  void* ws, hipStream_t s) {
+                  void* ws, const TileEntry* tab, hipStream_t s) {
   const int ntq = (Nq + kBM - 1) / kBM;
   const int G = ntq * H * plan.splits;
   const float c = scale * kLog2e;
@@ -476,8 +595,8 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int N
     opart = reinterpret_cast<float*>(ws);
     ml = reinterpret_cast<float2*>(opart + (size_t)plan.splits * H * Nq * D);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(G), dim3(kThreads), 0, s, q, k, v, Nq, Nk,
-                     H, c, out, lse, opart, ml, plan.splits, plan.keys_per_split);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, SEG>), dim3(G), dim3(kThreads), 0, s, q, k, v, Nq, Nk,
+                     H, c, out, lse, opart, ml, plan.splits, plan.keys_per_split, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   const int rows = H * Nq;
@@ -513,8 +632,31 @@ size_t attention_ws_bytes(const AttnPlan& p, int Nq, int H, int D) {
 hipError_t attention_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int Nq,
                             int Nk, int H, int D, float scale, uint16_t* out, float* lse,
                             const AttnPlan& plan, void* ws, hipStream_t s) {
-  return (D == 128) ? launch<128>(q, k, v, Nq, Nk, H, scale, out, lse, plan, ws, s)
-                    : launch<64>(q, k, v, Nq, Nk, H, scale, out, lse, plan, ws, s);
+  return (D == 128) ? launch<128, false>(q, k, v, Nq, Nk, H, scale, out, lse, plan, ws, nullptr, s)
+                    : launch<64, false>(q, k, v, Nq, Nk, H, scale, out, lse, plan, ws, nullptr, s);
+}
+
+size_t attention_window_table_bytes(int ntiles) {
+  return ((size_t)ntiles * sizeof(TileEntry) + 255) / 256 * 256;
+}
+
+// The window in place: the tile table goes at the start of ws, the split
+// partials after it. Nk is the padded key count of the pieces.
+hipError_t attention_window_launch(const uint16_t* q, const WinPieces& w, int Nq, int H, int D,
+                                   float scale, uint16_t* out, float* lse, const AttnPlan& plan,
+                                   void* ws, hipStream_t s) {
+  const int ntiles = w.tile0[w.npieces];
+  const int Nk = ntiles * kBN;
+  TileEntry* tab = reinterpret_cast<TileEntry*>(ws);
+  hipLaunchKernelGGL(attn_tile_table_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, s, w,
+                     (int64_t)H * D, tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void* part = static_cast<char*>(ws) + attention_window_table_bytes(ntiles);
+  return (D == 128) ? launch<128, true>(q, nullptr, nullptr, Nq, Nk, H, scale, out, lse, plan,
+                                        part, tab, s)
+                    : launch<64, true>(q, nullptr, nullptr, Nq, Nk, H, scale, out, lse, plan,
+                                       part, tab, s);
 }
 
 }  // namespace wkv

@@ -108,4 +108,26 @@ hipError_t attention_launch(const uint16_t* q, const uint16_t* k, const uint16_t
                             int Nq, int Nk, int H, int D, float scale, uint16_t* out,
                             float* lse, const AttnPlan& plan, void* ws, hipStream_t s);
 
+// The window read in place: its pieces (sink, retrieved bank chunks, recent
+// segments, current) in window order, each padded to whole 64-key tiles.
+// Piece p covers tiles [tile0[p], tile0[p+1]) and n[p] rows; a piece with
+// slot[p] >= 0 is bank chunk idx[slot[p]] (k[p], v[p] then hold the bank
+// base, and an id outside [0, M) reads as zero rows).
+constexpr int kMaxWinPieces = 32;
+struct WinPieces {
+  const uint16_t* k[kMaxWinPieces];
+  const uint16_t* v[kMaxWinPieces];
+  int32_t n[kMaxWinPieces];
+  int32_t slot[kMaxWinPieces];
+  int32_t tile0[kMaxWinPieces + 1];
+  const int32_t* idx;
+  int32_t M, Lc, npieces;
+};
+// ws holds the per-tile table (attention_window_table_bytes) and then the
+// split partials (attention_ws_bytes).
+size_t attention_window_table_bytes(int ntiles);
+hipError_t attention_window_launch(const uint16_t* q, const WinPieces& w, int Nq, int H, int D,
+                                   float scale, uint16_t* out, float* lse, const AttnPlan& plan,
+                                   void* ws, hipStream_t s);
+
 }  // namespace wkv

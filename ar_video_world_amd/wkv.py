@@ -111,13 +111,19 @@ _assemble = _sig("wkv_assemble_window", C.c_int,
 _attn_ws = _sig("wkv_attention_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
 _attn = _sig("wkv_chunk_attention", C.c_int,
              [_P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P])
+_attn_win_ws = _sig("wkv_attention_window_workspace_bytes", _SZ, [_I32, _I64, _I32, _I32])
+_attn_win = _sig("wkv_chunk_attention_window", C.c_int,
+                 [_P, _I32, C.POINTER(wkv_segment), C.POINTER(wkv_bank), _P, _I32,
+                  C.POINTER(wkv_segment), _I32, C.POINTER(wkv_segment), _I32, _I32, _F,
+                  _P, _P, _P, _SZ, _P])
 
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
            "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_pose_extrapolate", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
            "wkv_tier_resolve",
-           "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention"]
+           "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention",
+           "wkv_attention_window_workspace_bytes", "wkv_chunk_attention_window"]
 
 
 def _check(fn: str, st: int):
@@ -529,4 +535,48 @@ def wkv_chunk_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     st = _attn(_ptr(q), _ptr(k), _ptr(v), Nq, Nk, H, D, float(scale), _ptr(out), _ptr(lse),
                _ptr(ws), ws.numel(), _stream(stream))
     _check("wkv_chunk_attention", st)
+    return out, lse
+
+
+def wkv_attention_window_workspace_bytes(Nq: int, Nk_pad: int, H: int, D: int) -> int:
+    """Workspace of wkv_chunk_attention_window: the tile table and the split
+    partials at the preferred split (Nk_pad: the window's padded key count)."""
+    return int(_attn_win_ws(Nq, Nk_pad, H, D))
+
+
+def wkv_chunk_attention_window(q: torch.Tensor, sink, bank, retrieved_idx: Optional[torch.Tensor],
+                               recent, current, scale: float = 0.0, out=None,
+                               want_lse: bool = False, lse=None, ws=None, stream=None):
+    """Attention of q [Nq, H, D] over the window sink | retrieved | recent |
+    current read in place (no window copy); arguments as for
+    wkv_assemble_window (bf16 bank only) and wkv_chunk_attention.
+    Returns (out bf16 [Nq, H, D], lse float32 [H, Nq] or None)."""
+    _bits(q, "q")
+    Nq, H, D = q.shape
+    sk = _seg(sink)
+    cur = _seg(current)
+    rec_list = list(recent or [])
+    rec = (wkv_segment * max(len(rec_list), 1))(*[_seg(p) for p in rec_list])
+    n_ret = 0 if retrieved_idx is None else int(retrieved_idx.numel())
+    bk = wkv_bank(0, 0, 0, None, None, None, None)
+    if bank is not None and n_ret > 0:
+        int4 = "k_scale" in bank and bank["k_scale"] is not None
+        bk.dtype = WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16
+        bk.M, bk.Lc = int(bank["k"].shape[0]), int(bank["k"].shape[1])
+        bk.k, bk.v = bank["k"].data_ptr(), bank["v"].data_ptr()
+    Lc = bk.Lc if n_ret > 0 else 0
+    lens = [sk.n] + [Lc] * n_ret + [int(p[0].shape[0]) for p in rec_list] + [cur.n]
+    nk_pad = sum(64 * ((n + 63) // 64) for n in lens)
+    dev = q.device
+    if out is None:
+        out = torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((H, Nq), dtype=torch.float32, device=dev)
+    if ws is None:
+        nb = wkv_attention_window_workspace_bytes(Nq, nk_pad, H, D)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    st = _attn_win(_ptr(q), Nq, C.byref(sk), C.byref(bk), _ptr(retrieved_idx), n_ret, rec,
+                   len(rec_list), C.byref(cur), H, D, float(scale), _ptr(out), _ptr(lse),
+                   _ptr(ws), ws.numel(), _stream(stream))
+    _check("wkv_chunk_attention_window", st)
     return out, lse

@@ -386,6 +386,50 @@ def main():
                   "query_topk_us": round(t_tk * 1e3, 2)}
             del km_bank, mws
 
+        # ---- the window read in place (bf16 banks): the same serial steps
+        # with wkv_chunk_attention_window in place of assembly + attention,
+        # on the same sets; and that attention call alone, event-timed
+        inplace = None
+        if not c["int4"]:
+            nk_pad = sum(64 * ((n + 63) // 64) for n in [FT] + [Lc] * k + [FT] * nrec + [FT])
+            wws = torch.empty(max(w.wkv_attention_window_workspace_bytes(Nq, nk_pad, H, D), 256),
+                              dtype=torch.uint8, device=dev)
+
+            def step_in_place(i, ev=None):
+                s = sets[i % len(sets)]
+                w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                     kept_idx=s["kidx"], ws=cws, score_mode=a.score_mode)
+                idx, _, _ = w.wkv_pose_topk(poses, qhist, k, want_dist=False)
+                for j in range(nsteps):
+                    if ev is not None:
+                        ev[2 * j].record()
+                    w.wkv_chunk_attention_window(s["q"][j], s["sink"], bank, idx, s["recent"],
+                                                 s["cur"], out=s["out"], ws=wws)
+                    if ev is not None:
+                        ev[2 * j + 1].record()
+
+            for i in range(a.warmup):
+                step_in_place(i)
+            torch.cuda.synchronize()
+            t4 = time.perf_counter()
+            for i in range(a.steps):
+                step_in_place(i)
+            torch.cuda.synchronize()
+            t5 = time.perf_counter()
+            iev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nsteps)]
+                   for _ in range(a.steps)]
+            for i in range(a.steps):
+                step_in_place(i, iev[i])
+            torch.cuda.synchronize()
+            t_win = statistics.fmean(e[2 * j].elapsed_time(e[2 * j + 1]) for e in iev
+                                     for j in range(nsteps))
+            inplace = {"serial_ms_per_step": round((t5 - t4) / a.steps * 1e3, 4),
+                       "attention_window_us": round(t_win * 1e3, 2),
+                       "attention_window_TFLOPs": round(4.0 * Nq * Nk * D * H / (t_win * 1e-3)
+                                                        / 1e12, 1),
+                       "padded_keys": nk_pad}
+            del wws
+
         # ---- pose top-k with full rotations (the walk's yaw as z-axis
         # quaternions), timed on its own
         P8 = torch.zeros((M, 8), dtype=torch.float32, device=dev)
@@ -477,6 +521,7 @@ def main():
                                for name, v in (("compress", t_comp), ("pose_topk", t_pose),
                                                ("assemble", t_asm), ("attention", t_att))},
             "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+            "window_in_place": inplace,
         },
         "roofline": {
             "kernel": "wkv_chunk_attention" + (" (fwd + split merge)" if splits else ""),

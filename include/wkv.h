@@ -405,6 +405,46 @@ wkv_status wkv_chunk_attention(const uint16_t* q, const uint16_t* k,
                                uint16_t* out, float* lse, void* ws,
                                size_t ws_bytes, wkv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Chunk attention over the window read in place ([WorldAttention] kernel
+ * section: the contiguous KV copy before attention is a large share of its
+ * latency; [WorldKV] Sec. 4.2 / 5.1: the window is sink | retrieval | recent
+ * | denoising). Computes what wkv_assemble_window followed by
+ * wkv_chunk_attention computes, without writing the window: the kernel reads
+ * each 64-key tile straight from its piece (the sink, bank chunk
+ * retrieved_idx[i], a recent segment, or the current chunk).
+ *   q, Nq, H, D, scale, out, lse   as for wkv_chunk_attention
+ *   sink, bank, retrieved_idx, n_ret, recent, n_recent, current
+ *                                  as for wkv_assemble_window; the bank
+ *                                  must be WKV_BANK_BF16 (an int4 bank is
+ *                                  WKV_ERR_UNSUPPORTED: its rows need the
+ *                                  dequantising gather). A retrieved id
+ *                                  outside [0, M) reads as zero rows, as in
+ *                                  the assembled window.
+ *   ws, ws_bytes   device workspace: a table of the window's 64-key tiles
+ *                  (64 bytes per tile, rounded up to 256 bytes; required,
+ *                  WKV_ERR_WORKSPACE otherwise), then split-key partials.
+ *                  wkv_attention_window_workspace_bytes() gives the size
+ *                  with the preferred split; with less, fewer splits. The
+ *                  call writes the table on its stream, so concurrent calls
+ *                  need separate workspaces.
+ * Each piece is padded to whole 64-key tiles and its padding is masked, so
+ * the result equals the assembled path's up to the order of the fp32
+ * additions. Limits: at most 32 pieces (n_ret + n_recent + 2), the padded
+ * key count Nk_pad = sum of 64 * ceil(n / 64) over the pieces is >= 1 and
+ * Nk_pad * H * D < 2^31.
+ * ------------------------------------------------------------------------ */
+size_t wkv_attention_window_workspace_bytes(int32_t Nq, int64_t Nk_pad, int32_t H,
+                                            int32_t D);
+
+wkv_status wkv_chunk_attention_window(const uint16_t* q, int32_t Nq,
+                                      const wkv_segment* sink, const wkv_bank* bank,
+                                      const int32_t* retrieved_idx, int32_t n_ret,
+                                      const wkv_segment* recent, int32_t n_recent,
+                                      const wkv_segment* current, int32_t H, int32_t D,
+                                      float scale, uint16_t* out, float* lse, void* ws,
+                                      size_t ws_bytes, wkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -243,3 +243,34 @@ def test_assemble_window_row_cap(w):
     # 2^25 + 2^25 rows = 2^26 > 2^26 - 1
     assert f(R(big), R(bank), A, 0, rec, 1, R(cur), 2, 64, A, A, 1 << 27, None) == 2
     assert "exceeds" in w.wkv_last_error()
+
+
+def test_attention_window_validation(w):
+    f = w._attn_win
+    R = C.byref
+    seg = w.wkv_segment(A, A, 10)
+    empty = w.wkv_segment(None, None, 0)
+    bank = w.wkv_bank(0, 4, 8, A, A, None, None)
+    bank_i4 = w.wkv_bank(1, 4, 8, A, A, A, A)
+    rec = (w.wkv_segment * 2)(seg, seg)
+    args = lambda **kw: dict(dict(q=A, Nq=5, sink=R(seg), bank=R(bank), idx=A, n_ret=2, rec=rec,
+                                  n_rec=2, cur=R(seg), H=2, D=64, scale=0.0, out=A, lse=None,
+                                  ws=None, wsb=0, s=None), **kw)
+    call = lambda **kw: f(*args(**kw).values())
+    assert call(q=None) == 1
+    assert call(sink=None) == 1
+    assert call(D=96) == 7
+    assert call(Nq=0) == 2
+    assert call(n_ret=-1) == 2
+    assert call(n_ret=20, n_rec=11) == 2          # more than 32 pieces
+    assert call(idx=None) == 1
+    assert call(bank=R(bank_i4)) == 7             # an int4 bank needs the assembling gather
+    assert "int4" in w.wkv_last_error()
+    assert call(q=MIS) == 5
+    assert call(sink=R(empty), n_ret=0, n_rec=0, cur=R(empty)) == 2   # empty window
+    assert call(scale=float("nan")) == 2
+    assert call() == 6                            # no workspace for the tile table
+    assert "tile table" in w.wkv_last_error()
+    assert call(ws=A, wsb=255) == 6               # the table needs at least 256 bytes
+    assert w._attn_win_ws(5, 640, 2, 64) >= 256
+    assert w._attn_win_ws(0, 640, 2, 64) == 0
