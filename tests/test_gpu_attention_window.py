@@ -7,7 +7,8 @@ the library's own two-call path (wkv_assemble_window, then
 wkv_chunk_attention) must agree with it to the same tolerance. Pieces of
 every length class are covered: whole tiles, ragged tails, single rows,
 empty pieces, out-of-range bank ids (zero rows, as in the assembled window),
-fewer splits than preferred, and the full 1.3B-class window on sampled rows."""
+fewer splits than preferred, and the full 1.3B- and 14B-class windows on
+sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +103,10 @@ def test_13b_window_sampled(w):
     rows = np.unique(np.concatenate([rng.integers(0, 2640, 190), np.arange(2560, 2640, 7)]))
     window_case(w, 12, 128, 2640, 1760, 20, [3, 9, 17], [2640, 2640], 2640, 2640,
                 "1.3B-class window", sample=rows)
+
+
+def test_14b_window_sampled(w):
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([rng.integers(0, 4680, 40), np.arange(4608, 4680, 9)]))
+    window_case(w, 40, 128, 4680, 2340, 12, [0, 2, 5, 7, 10, 11], [4680, 4680], 4680, 4680,
+                "14B-class window (12-chunk bank slice)", sample=rows)
