@@ -41,6 +41,12 @@
 //   * Blocks are renumbered so that each XCD (blocks are dealt round-robin
 //     over the 8 XCDs) works on a contiguous range of (head, split, q-tile):
 //     tiles sharing K/V share that XCD's L2.
+//   * The same kernel also reads the window in place (WorldAttention's
+//     kernel section counts the contiguous KV copy among its main costs):
+//     the window's pieces (sink, retrieved bank chunks, recent segments,
+//     current) are padded to whole tiles, a small kernel writes one entry per
+//     tile (its rows in K and V, and its real keys), and the key loop takes
+//     each tile's loads from that entry instead of from one contiguous array.
 #include <cstring>
 
 #include "wkv_common.hpp"
@@ -139,8 +145,6 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// SEG: the keys are the window's pieces read in place (WinPieces), each
-// padded to whole tiles; Nk is then the padded key count, a multiple of 64.
 // One 64-key tile t of the window read in place, as two 32-byte halves. The
 // first holds what iteration t of the key loop needs in one scalar load: the
 // K rows of tile t+2 and the V rows of tile t+1 (head 0; the loop queues
@@ -209,6 +213,9 @@ __global__ __launch_bounds__(256) void attn_tile_table_kernel(const WinPieces wi
   tab[t] = e;
 }
 
+// SEG: the keys are the window's pieces read in place, each padded to whole
+// tiles and described per tile by `tab`; Nk is then the padded key count, a
+// multiple of 64. Otherwise K and V are one contiguous window.
 template <int D, bool SEG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
