@@ -3,7 +3,9 @@ streams (compression of the evicted chunk into the bank, then pose retrieval,
 on a side stream; assembly and attention on the main stream, ordered by
 events) gives bitwise the same windows, outputs and bank as the same calls on
 one stream. Each step's compression writes the bank slot that later
-retrievals may pick, so the side stream waits for the previous assembly."""
+retrievals may pick, so the side stream waits for the previous assembly (or,
+with the window read in place, for the previous attention, which reads the
+bank itself). The in-place path is checked the same way."""
 import pytest
 import torch
 
@@ -16,7 +18,8 @@ pytestmark = [pytest.mark.gpu,
 DEV = "cuda:0"
 
 
-def test_two_streams_match_one():
+@pytest.mark.parametrize("in_place", [False, True])
+def test_two_streams_match_one(in_place):
     import ar_video_world_amd.wkv as w
     F, T, H, D, r, M, k, steps = 3, 128, 4, 128, 0.5, 6, 2, 8
     FT = F * T
@@ -41,6 +44,9 @@ def test_two_streams_match_one():
         wk = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=DEV)
         wv = torch.empty_like(wk)
         outs = [torch.empty((FT, H, D), dtype=torch.bfloat16, device=DEV) for _ in range(steps)]
+        nk_pad = sum(64 * ((n + 63) // 64) for n in (FT, Lc, Lc, FT, FT))
+        wws = torch.empty(w.wkv_attention_window_workspace_bytes(FT, nk_pad, H, D),
+                          dtype=torch.uint8, device=DEV)
         wins = []
         ready = [torch.cuda.Event() for _ in range(2)]
         assembled = torch.cuda.Event()
@@ -60,6 +66,12 @@ def test_two_streams_match_one():
         def back(i):
             with torch.cuda.stream(main):
                 main.wait_event(ready[i % 2])
+                if in_place:
+                    wins.append(ridx[i % 2].clone())
+                    w.wkv_chunk_attention_window(qs[i], segs[0], bank, ridx[i % 2], [segs[1]],
+                                                 segs[2], out=outs[i], ws=wws)
+                    assembled.record(main)
+                    return
                 w.wkv_assemble_window(segs[0], bank, ridx[i % 2], [segs[1]], segs[2], H, D,
                                       win_k=wk, win_v=wv)
                 assembled.record(main)
@@ -74,9 +86,9 @@ def test_two_streams_match_one():
         torch.cuda.synchronize()
         return outs, wins, bk, bv
 
-    say("pipeline", "one stream")
+    say("pipeline", "one stream", "in place" if in_place else "assembled")
     o1, i1, k1, v1 = run(False)
-    say("pipeline", "two streams")
+    say("pipeline", "two streams", "in place" if in_place else "assembled")
     o2, i2, k2, v2 = run(True)
     for i in range(steps):
         assert torch.equal(i1[i], i2[i]), i
