@@ -88,7 +88,7 @@ CompressWsLayout compress_ws_layout(int32_t B, int32_t F, int32_t T, int32_t H, 
   CompressWsLayout L{};
   L.scores = 0;
   L.part = scores_in_ws ? round_up((size_t)B * (size_t)(F - 1) * (size_t)T * sizeof(double)) : 0;
-  L.abar = L.part + (mean ? round_up((size_t)B * H * wkv::compress_mean_slices(T) * D * sizeof(double)) : 0);
+  L.abar = L.part + (mean ? round_up((size_t)B * H * wkv::compress_mean_slices(B, T, H) * D * sizeof(double)) : 0);
   L.total = L.abar + (mean ? round_up((size_t)B * H * D * sizeof(double)) : 0);
   return L;
 }

@@ -171,25 +171,52 @@ __device__ __forceinline__ void store_slice(const uint4 (&a)[NLD], size_t e0, in
   }
 }
 
-// grid: (ceil(T / kMeanTok), H, B). Sum over a slice of anchor tokens of the
-// unit anchor keys of one head (a zero key adds nothing), float64, into
-// part[b][h][slice][D]; copies those anchor rows to k_out. 4 lanes own one
-// row slice of D elements, as in the score kernel.
-constexpr int kMeanTok = 128;
+// Anchor-mean blocks: 256 lanes, or 512 when 256 would leave over an eighth
+// more of the quads idle (40 heads: 40 of 64 quads against 120 of 128) or
+// cannot hold one quad per head.
+int mean_block_threads(int H) {
+  const int w256 = H <= 64 ? 64 % H : 64, w512 = 128 % H;
+  return 2 * w256 > w512 + 16 ? 512 : 256;
+}
 
-template <int D, bool Q4>
-__global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
-    const uint16_t* __restrict__ k, int F, int T, int H, double* __restrict__ part,
+// Anchor tokens per anchor-mean block: whole passes, doubled while a unit has
+// more than 128 slices (the finalize kernel adds them in sequence) or the grid
+// keeps >= 2048 blocks at twice the size.
+int compress_mean_tokens(int B, int T, int H) {
+  int mt = mean_block_threads(H) / kLanesPerPair / H;
+  while (mt < T && ((T + mt - 1) / mt > 128 ||
+                    (long long)B * ((T + 2 * mt - 1) / (2 * mt)) >= 2048))
+    mt *= 2;
+  return mt;
+}
+
+// grid: (nslice, B), block NT. Sum over a slice of mt anchor tokens of the
+// unit anchor keys of every head (a zero key adds nothing), float64, into
+// part[b][h][slice][D]; copies those anchor rows to k_out. 4 lanes own one
+// (token, head) row slice of D elements, as in the score kernel, and each quad
+// keeps one head: quad q takes head q % H of token q / H of every pass of
+// P = (NT/4) / H consecutive tokens. The quads of a pass therefore cover
+// whole rows, so the int4 codes and scales of a token leave as full cache
+// lines (a block per head wrote 64-byte and 8-byte pieces of lines shared
+// with other heads' blocks: 465 against 325 us for the bf16 store on 300
+// units of 3 x 880 x 12 x 128). The P quads of a head add into LDS in a fixed
+// order, so the result does not depend on timing.
+template <int D, bool Q4, int NT>
+__global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
+    const uint16_t* __restrict__ k, int F, int T, int H, int mt, double* __restrict__ part,
     CompressOut out, int Lc) {
   constexpr int NLD = D / 32;
   constexpr int E = NLD * 8;  // elements per lane
-  __shared__ double red[kScoreBlock / 64][D];
-  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int j0 = sl * kMeanTok;
-  const int ntok = min(kMeanTok, T - j0);
+  constexpr int NQ = NT / kLanesPerPair;
+  extern __shared__ double red[];  // [H][D]
+  const int sl = blockIdx.x, b = blockIdx.y;
+  const int P = NQ / H;  // tokens per pass (H <= NQ)
+  const int j0 = sl * mt;
+  const int ntok = min(mt, T - j0);
   const int tid = threadIdx.x;
-  const int slot = tid / kLanesPerPair;
+  const int q = tid / kLanesPerPair;
   const int sub = tid % kLanesPerPair;
+  const int t = q / H, h = q - t * H;
   const size_t HD = (size_t)H * D;
   const uint16_t* unit = k + (size_t)b * F * T * HD;
   const size_t ubase = (size_t)b * Lc * HD;  // element offset of this unit's output
@@ -204,12 +231,13 @@ __global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
 #pragma unroll
     for (int i = 0; i < NLD; ++i) an[i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
   };
-  if (slot < ntok) load_row(slot);
-  for (int jl = slot; jl < ntok; jl += kPairsPerPass) {
+  const int first = t < P ? t : ntok;  // quads past the last full head set idle
+  if (first < ntok) load_row(first);
+  for (int jl = first; jl < ntok; jl += P) {
     uint4 a[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) a[i] = an[i];
-    if (jl + kPairsPerPass < ntok) load_row(jl + kPairsPerPass);
+    if (jl + P < ntok) load_row(jl + P);
     store_slice<NLD, Q4>(a, ubase + ((size_t)(j0 + jl) * H + h) * D, sub, out.k, out.kq, out.ks);
     double na = 0.0;
 #pragma unroll
@@ -220,33 +248,29 @@ __global__ __launch_bounds__(kScoreBlock) void compress_anchor_mean_kernel(
     for (int i = 0; i < NLD; ++i) {
       const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[i * 8 + 2 * q] = fma((double)bf16_to_f32(w[q] & 0xFFFFu), inv, acc[i * 8 + 2 * q]);
-        acc[i * 8 + 2 * q + 1] = fma((double)bf16_to_f32(w[q] >> 16), inv, acc[i * 8 + 2 * q + 1]);
+      for (int c = 0; c < 4; ++c) {
+        acc[i * 8 + 2 * c] = fma((double)bf16_to_f32(w[c] & 0xFFFFu), inv, acc[i * 8 + 2 * c]);
+        acc[i * 8 + 2 * c + 1] = fma((double)bf16_to_f32(w[c] >> 16), inv, acc[i * 8 + 2 * c + 1]);
       }
     }
   }
-  // Lanes with the same sub hold the same elements: butterfly over the 16
-  // quads of a wave, then a fixed-order sum over the waves.
+  // Pass slot 0 writes each head's D sums, slots 1..P-1 add theirs in turn.
+  for (int r = 0; r < P; ++r) {
+    if (t == r) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+      for (int i = 0; i < NLD; ++i)
 #pragma unroll
-    for (int o = 4; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+        for (int e = 0; e < 8; ++e) {
+          double* cell = red + h * D + i * 32 + sub * 8 + e;
+          *cell = (r == 0) ? acc[i * 8 + e] : *cell + acc[i * 8 + e];
+        }
+    }
+    __syncthreads();
   }
-  const int lane = tid & 63, wave = tid >> 6;
-  if (lane < kLanesPerPair) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][i * 32 + sub * 8 + e] = acc[i * 8 + e];
-  }
-  __syncthreads();
-  double* dst = part + (((size_t)b * H + h) * gridDim.x + sl) * D;
-  for (int d = tid; d < D; d += kScoreBlock) {
-    double t = red[0][d];
-#pragma unroll
-    for (int w = 1; w < kScoreBlock / 64; ++w) t += red[w][d];
-    dst[d] = t;
+  double* dst = part + (size_t)b * HD * gridDim.x;
+  for (int i = tid; i < (int)HD; i += NT) {
+    const int hh = i / D, d = i - hh * D;
+    dst[((size_t)hh * gridDim.x + sl) * D + d] = red[i];
   }
 }
 
@@ -255,8 +279,17 @@ __global__ void compress_anchor_mean_final_kernel(const double* __restrict__ par
                                                   int T, int H, double* __restrict__ abar) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, D = blockDim.x;
   const double* src = part + ((size_t)b * H + h) * nslice * D + d;
+  // Eight loads in flight per round; the sum still runs in slice order.
   double t = 0.0;
-  for (int s = 0; s < nslice; ++s) t += src[(size_t)s * D];
+  int s = 0;
+  for (; s + 8 <= nslice; s += 8) {
+    double x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = src[(size_t)(s + i) * D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += x[i];
+  }
+  for (; s < nslice; ++s) t += src[(size_t)s * D];
   abar[((size_t)b * H + h) * D + d] = t / (double)T;
 }
 
@@ -538,16 +571,27 @@ hipError_t dispatch_score_F(const uint16_t* k, int B, int F, int T, int H, int T
   }
 }
 
+template <int D, int NT>
+void launch_anchor_mean_nt(const uint16_t* k, int B, int F, int T, int H, double* part,
+                           const CompressOut& out, bool q4, int Lc, hipStream_t s) {
+  const int mt = compress_mean_tokens(B, T, H);
+  const dim3 grid((T + mt - 1) / mt, B);
+  const size_t lds = (size_t)H * D * sizeof(double);
+  if (q4)
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true, NT>), grid, dim3(NT), lds, s, k, F,
+                       T, H, mt, part, out, Lc);
+  else
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, false, NT>), grid, dim3(NT), lds, s, k,
+                       F, T, H, mt, part, out, Lc);
+}
+
 template <int D>
 void launch_anchor_mean(const uint16_t* k, int B, int F, int T, int H, double* part,
                         const CompressOut& out, bool q4, int Lc, hipStream_t s) {
-  const dim3 grid(compress_mean_slices(T), H, B);
-  if (q4)
-    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true>), grid, dim3(kScoreBlock), 0, s, k,
-                       F, T, H, part, out, Lc);
+  if (mean_block_threads(H) == 512)
+    launch_anchor_mean_nt<D, 512>(k, B, F, T, H, part, out, q4, Lc, s);
   else
-    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, false>), grid, dim3(kScoreBlock), 0, s,
-                       k, F, T, H, part, out, Lc);
+    launch_anchor_mean_nt<D, 256>(k, B, F, T, H, part, out, q4, Lc, s);
 }
 
 }  // namespace
@@ -569,7 +613,10 @@ int compress_score_tile(int B, int T, int H, bool grow) {
   return tt < T ? tt : T;
 }
 
-int compress_mean_slices(int T) { return (T + kMeanTok - 1) / kMeanTok; }
+int compress_mean_slices(int B, int T, int H) {
+  const int mt = compress_mean_tokens(B, T, H);
+  return (T + mt - 1) / mt;
+}
 
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4) {
   const int TT = compress_score_tile(B, T, H, q4 || mean);
@@ -589,7 +636,7 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
   hipError_t e = hipSuccess;
   if (score) {
     if (abar) {
-      const int ns = compress_mean_slices(T);
+      const int ns = compress_mean_slices(B, T, H);
       if (D == 128)
         launch_anchor_mean<128>(k, B, F, T, H, mean_part, out, q4, Lc, s);
       else

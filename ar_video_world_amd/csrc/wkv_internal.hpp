@@ -13,7 +13,7 @@ constexpr int64_t kMaxWindowRows = (1LL << 26) - 1;  // one 64-lane block per ro
 
 // ---- compression
 int compress_score_tile(int B, int T, int H, bool grow);
-int compress_mean_slices(int T);  // anchor-token slices of the anchor-mean sums
+int compress_mean_slices(int B, int T, int H);  // anchor-token slices of the anchor-mean sums
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4);
 // Destination of the compressed rows: bf16 rows (k, v) when k_packed is
 // null, else int4 codes (k_packed, v_packed: [B][Lc][H][D/2]) with bf16 group

@@ -48,9 +48,10 @@ def test_abi_version_and_keep_count(w):
     assert w.wkv_keep_count(3, 7, 1.5) == -1
     assert w.wkv_keep_count(1, 7, 0.5) == -1
     assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128) == 4 * 1760 * 8
-    # anchor-mean: + partial sums [B][H][ceil(T/128)][D] + abar [B][H][D], float64
+    # anchor-mean: + partial sums [B][H][slices][D] + abar [B][H][D], float64;
+    # 4 units of 880 anchor tokens at 12 heads take 88 slices of 10 tokens
     assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, "anchor_mean") == \
-        4 * 1760 * 8 + 4 * 12 * 7 * 128 * 8 + 4 * 12 * 128 * 8
+        4 * 1760 * 8 + 4 * 12 * 88 * 128 * 8 + 4 * 12 * 128 * 8
     assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, 2) == 0
     assert w.wkv_attention_workspace_bytes(0, 1, 1, 128) == 0
 

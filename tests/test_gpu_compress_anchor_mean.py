@@ -49,7 +49,9 @@ def test_sweep_batch(w):
 
 
 @pytest.mark.parametrize("F,T,H,D", [(2, 100, 3, 128), (4, 37, 5, 64), (3, 1, 1, 64),
-                                     (3, 129, 2, 128), (2, 257, 4, 64), (3, 128, 1, 128)])
+                                     (3, 129, 2, 128), (2, 257, 4, 64), (3, 128, 1, 128),
+                                     (3, 50, 40, 128), (2, 23, 64, 128), (2, 11, 128, 64),
+                                     (3, 70, 24, 64), (2, 1000, 7, 64)])
 def test_ragged_shapes(w, F, T, H, D):
     K, V = gen_units(7, 2, F, T, H, D)
     run_case(w, K, V, F, T, 0.5, f"am ragged F={F} T={T} H={H} D={D}", score_mode=MODE)

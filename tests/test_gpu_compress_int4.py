@@ -82,7 +82,8 @@ def test_batch_without_scores(w):
 
 
 @pytest.mark.parametrize("F,T,H,D", [(2, 100, 3, 128), (4, 37, 5, 64), (3, 1, 1, 64),
-                                     (3, 129, 2, 128)])
+                                     (3, 129, 2, 128), (3, 50, 40, 128), (2, 23, 64, 128),
+                                     (2, 11, 128, 64), (3, 70, 24, 64)])
 @pytest.mark.parametrize("mode", ["position", "anchor_mean"])
 def test_ragged_shapes(w, F, T, H, D, mode):
     K, V = gen_units(7, 2, F, T, H, D)
