@@ -97,3 +97,11 @@ def test_modes_differ_but_share_the_anchor_rows(w):
     assert not torch.equal(p[3], a[3])
     assert np.array_equal(np_bits(p[0][:256]), np_bits(a[0][:256]))
     assert np.array_equal(np_bits(a[0][:256]), np_bits(K[0][:256]))
+
+
+def test_many_units_grow_runs(w):
+    """300 units of 64 anchor tokens at 12 heads: the anchor-mean blocks take
+    runs of 10 tokens (two passes of 5, the grid kept >= 2048 blocks), and
+    each unit's last run is 4 tokens long."""
+    K, V = gen_units(5, 300, 3, 64, 12, 64)
+    run_case(w, K, V, 3, 64, 0.5, "am 300 units", score_mode=MODE)

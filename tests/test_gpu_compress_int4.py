@@ -122,3 +122,10 @@ def test_matches_bf16_path_after_quantisation(w):
         rv, rvs = O.int4_quantize(np_bits(vo[b]))
         assert np.array_equal(kp[b].cpu().numpy(), rk) and np.array_equal(np_bits(ks[b]), rks)
         assert np.array_equal(vp[b].cpu().numpy(), rv) and np.array_equal(np_bits(vs[b]), rvs)
+
+
+def test_many_units_grow_runs_anchor_mean(w):
+    """300 units of 64 anchor tokens at 12 heads, anchor-mean score: the
+    anchor rows are encoded by blocks of 10-token runs, the last one 4 long."""
+    K, V = gen_units(5, 300, 3, 64, 12, 64)
+    run_int4(w, K, V, 3, 64, 0.5, "int4 am 300 units", score_mode="anchor_mean")
