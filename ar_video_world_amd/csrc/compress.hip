@@ -14,10 +14,10 @@
 //            score kernel also writes the anchor rows of k_out.
 //            With the anchor-mean score (the section's equation: the mean
 //            cosine to all T anchor tokens) two kernels run first instead:
-//            anchor-mean sums, per (anchor-token slice, head), the unit
-//            anchor keys k/|k| in float64 and writes those anchor rows of
-//            k_out; a finalize kernel adds the slices in a fixed order and
-//            divides by T. The mean of the cosines to every anchor token
+//            anchor-mean sums, per run of anchor tokens of one unit (all
+//            heads, so rows are written whole), the unit anchor keys k/|k|
+//            in float64 and writes those anchor rows of k_out; a finalize
+//            kernel adds the runs in a fixed order and divides by T. The mean of the cosines to every anchor token
 //            is then one dot product, <k, abar> / |k|, so the score kernel
 //            reads only the non-anchor rows and abar (kept in LDS).
 //   select - one block per unit, sized to the pooled count (512 threads x 4
@@ -25,9 +25,9 @@
 //            (score, index) key, stable compaction by block scan, writes
 //            kept_idx.
 //   gather - one wave per output row: copies the kept K rows (non-anchor) and
-//            all kept V rows with 16-byte loads and stores. Outputs and V
-//            (read once) use streaming accesses; the kept K rows use the
-//            default policy since the score pass has just read them.
+//            all kept V rows with 16-byte loads and stores, all streaming
+//            (plain loads of the K rows, which the score pass read before,
+//            were 2 % slower).
 #include "wkv_common.hpp"
 #include "wkv_internal.hpp"
 #include "wkv_select.hpp"
