@@ -566,19 +566,37 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   if (rowid >= H * Nq) return;
   const int h = rowid / Nq, q = rowid - h * Nq;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mlpart[((size_t)s * H + h) * Nq + q].x);
   float acc[PER];
+  float den;
+  if (nsplit == 2) {
+    // Two splits (the usual case): every load of the row is in flight at once.
+    const size_t r0 = (size_t)h * Nq + q, r1 = ((size_t)H + h) * Nq + q;
+    const float2 m0 = mlpart[r0], m1 = mlpart[r1];
+    float x0[PER], x1[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float den = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t row = ((size_t)s * H + h) * Nq + q;
-    const float2 ml = mlpart[row];
-    const float w = exp2f(ml.x - M);
-    den += w * ml.y;
-    const float* pp = opart + row * D + sub * PER;
+    for (int i = 0; i < PER; ++i) {
+      x0[i] = opart[r0 * D + sub * PER + i];
+      x1[i] = opart[r1 * D + sub * PER + i];
+    }
+    M = fmaxf(m0.x, m1.x);
+    const float w0 = exp2f(m0.x - M), w1 = exp2f(m1.x - M);
+    den = fmaf(w1, m1.y, w0 * m0.y);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * pp[i];
+    for (int i = 0; i < PER; ++i) acc[i] = fmaf(w1, x1[i], w0 * x0[i]);
+  } else {
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mlpart[((size_t)s * H + h) * Nq + q].x);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t row = ((size_t)s * H + h) * Nq + q;
+      const float2 ml = mlpart[row];
+      const float w = exp2f(ml.x - M);
+      den = fmaf(w, ml.y, den);
+      const float* pp = opart + row * D + sub * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, pp[i], acc[i]);
+    }
   }
   const float inv = 1.0f / den;
   uint16_t* op = O + (size_t)q * H * D + (size_t)h * D + sub * PER;
