@@ -52,6 +52,10 @@ def test_abi_version_and_keep_count(w):
     # 4 units of 880 anchor tokens at 12 heads take 88 slices of 10 tokens
     assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, "anchor_mean") == \
         4 * 1760 * 8 + 4 * 12 * 88 * 128 * 8 + 4 * 12 * 128 * 8
+    # 40 heads take 512-lane blocks (3 tokens a pass); one unit of 1560 anchor
+    # tokens doubles the run to 24 tokens (65 runs, the first count <= 128)
+    assert w.wkv_compress_workspace_bytes(1, 3, 1560, 40, 128, "anchor_mean") == \
+        25088 + 40 * 65 * 128 * 8 + 40 * 128 * 8
     assert w.wkv_compress_workspace_bytes(4, 3, 880, 12, 128, 2) == 0
     assert w.wkv_attention_workspace_bytes(0, 1, 1, 128) == 0
 
