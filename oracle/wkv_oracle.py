@@ -21,7 +21,7 @@ Sources (cited by page title and section):
   squared-L2 translation + geodesic rotation, each normalised over the
   candidate set).
 * "WorldPager" (thelatestinai summary): abstract and Fig. 2 (int4 KV store;
-  retrieval set of the next chunk from the extrapolated camera pose).
+  next-chunk retrieval driven by a linearly extrapolated pose).
 * WorldAttention breakdown (pinghaoyang.com.cn): "from video attention to long
   interaction" (scaled dot-product attention of the current chunk's queries
   over the visible keys, 1/sqrt(d) scaling) and the custom-kernel section
@@ -302,9 +302,9 @@ def pose_topk_so3(poses, query, k: int):
 
 
 def pose_extrapolate(prev, last) -> np.ndarray:
-    """Linear pose extrapolation for the next chunk's retrieval (WorldPager
-    Fig. 2: the retrieval set of chunk c+1 is computed from the extrapolated
-    camera pose). q = last + (last - prev) in float64, yaw wrapped, stored as
+    """Query pose one chunk ahead, by linear extrapolation of the last two
+    poses (WorldPager Fig. 2: next-chunk retrieval runs on an extrapolated
+    pose). q = last + (last - prev) in float64, yaw wrapped, stored as
     float32."""
     p = np.asarray(prev, dtype=np.float32).astype(np.float64)
     l = np.asarray(last, dtype=np.float32).astype(np.float64)
@@ -384,7 +384,8 @@ def compress_chunk_int4(k_bits, v_bits, F: int, T: int, r: float, score_mode: st
 def mean_rows(x_bits, rows=None) -> np.ndarray:
     """Mean over token rows, float64. x_bits: bf16 bits [B][L_in][H][D] (or
     [L_in][H][D]); rows: optional int array [B][L] (or [L]) naming the rows
-    averaged (default: all L_in). Returns [B][H][D] (or [H][D])."""
+    averaged (default: all L_in). A row id outside [0, L_in) names no row: it
+    adds a zero row and still counts in the 1/L. Returns [B][H][D] (or [H][D])."""
     X = bf16_to_f64(x_bits)
     single = X.ndim == 3
     if single:
@@ -392,7 +393,14 @@ def mean_rows(x_bits, rows=None) -> np.ndarray:
     if rows is not None:
         r = np.asarray(rows, dtype=np.int64)
         r = r[None] if r.ndim == 1 else r
-        X = np.stack([X[b][r[b]] for b in range(X.shape[0])])
+        L_in = X.shape[1]
+        picked = []
+        for b in range(X.shape[0]):
+            ok = (r[b] >= 0) & (r[b] < L_in)
+            xb = np.zeros((r.shape[1],) + X.shape[2:], dtype=np.float64)
+            xb[ok] = X[b][r[b][ok]]
+            picked.append(xb)
+        X = np.stack(picked)
     m = np.sum(X, axis=1) / X.shape[1]
     return m[0] if single else m
 
@@ -503,15 +511,20 @@ def assemble_window(sink, bank, idx, recent, current):
     attention window without re-encoding; Sec. 5.1 gives the partition sink /
     retrieval / recent / denoising. Each argument is a (k, v) pair of bf16
     bit arrays [n][H][D]; ``bank`` is (k, v) [M][Lc][H][D]; ``idx`` are the
-    retrieved chunk ids (ascending). Returns (win_k, win_v).
+    retrieved chunk ids (ascending). An id outside [0, M) names no stored
+    chunk and contributes Lc zero rows. Returns (win_k, win_v).
     """
     parts_k = [np.asarray(sink[0]).view(np.uint16)]
     parts_v = [np.asarray(sink[1]).view(np.uint16)]
     bk = np.asarray(bank[0]).view(np.uint16)
     bv = np.asarray(bank[1]).view(np.uint16)
     for i in idx:
-        parts_k.append(bk[int(i)])
-        parts_v.append(bv[int(i)])
+        if 0 <= int(i) < bk.shape[0]:
+            parts_k.append(bk[int(i)])
+            parts_v.append(bv[int(i)])
+        else:
+            parts_k.append(np.zeros(bk.shape[1:], dtype=np.uint16))
+            parts_v.append(np.zeros(bv.shape[1:], dtype=np.uint16))
     for k, v in recent:
         parts_k.append(np.asarray(k).view(np.uint16))
         parts_v.append(np.asarray(v).view(np.uint16))
@@ -521,9 +534,19 @@ def assemble_window(sink, bank, idx, recent, current):
 
 
 def dequant_bank_chunks(packed_k, packed_v, scale_k, scale_v, idx):
-    """bf16 bit rows of the listed int4 bank chunks: (k [n][Lc][H][D], v ...)."""
-    ks = [int4_dequant(packed_k[int(i)], scale_k[int(i)]) for i in idx]
-    vs = [int4_dequant(packed_v[int(i)], scale_v[int(i)]) for i in idx]
+    """bf16 bit rows of the listed int4 bank chunks, in the order listed:
+    (k [n][Lc][H][D], v [n][Lc][H][D]), each chunk dequantised by int4_dequant.
+    An id outside [0, M) gives Lc zero rows, as in assemble_window."""
+    M = np.asarray(packed_k).shape[0]
+
+    def one(packed, scale, i):
+        if 0 <= int(i) < M:
+            return int4_dequant(packed[int(i)], scale[int(i)])
+        shp = np.asarray(packed).shape[1:-1] + (np.asarray(packed).shape[-1] * 2,)
+        return np.zeros(shp, dtype=np.uint16)
+
+    ks = [one(packed_k, scale_k, i) for i in idx]
+    vs = [one(packed_v, scale_v, i) for i in idx]
     return np.stack(ks), np.stack(vs)
 
 

@@ -178,6 +178,45 @@ def test_window_layout_and_offsets():
     assert np.array_equal(wv[24:], cur[1])
 
 
+def test_window_out_of_range_ids_give_zero_rows():
+    rng = np.random.default_rng(6)
+    H, D, Lc, M = 2, 64, 3, 4
+    bank = (rng.integers(1, 65535, (M, Lc, H, D), dtype=np.uint16),
+            rng.integers(1, 65535, (M, Lc, H, D), dtype=np.uint16))
+    sink = (bank[0][0][:1], bank[1][0][:1])
+    cur = (bank[0][1][:2], bank[1][1][:2])
+    wk, wv = O.assemble_window(sink, bank, [-1, 2, M], [], cur)
+    assert wk.shape == (1 + 3 * Lc + 2, H, D)
+    assert not wk[1:1 + Lc].any() and not wv[1:1 + Lc].any()          # id -1
+    assert np.array_equal(wk[1 + Lc:1 + 2 * Lc], bank[0][2])          # id 2
+    assert not wk[1 + 2 * Lc:1 + 3 * Lc].any() and not wv[1 + 2 * Lc:1 + 3 * Lc].any()  # id M
+    assert np.array_equal(wv[-2:], cur[1])
+
+
+def test_dequant_bank_chunks_by_hand():
+    # Three int4 chunks of Lc = 2 rows, 1 head, D = 64 (two groups of 32).
+    # chunk 0: every code 3, scales 0.5 -> every value 1.5 (bf16 0x3FC0)
+    # chunk 1: every code 1, group scales 0.5 | 2 -> 0.5 (0x3F00) | 2 (0x4000)
+    # chunk 2: codes -8 (even d) / 7 (odd d), scale 2 -> -16 (0xC180) / 14 (0x4160)
+    Lc, D = 2, 64
+    pk = np.empty((3, Lc, 1, D // 2), np.uint8)
+    sc = np.empty((3, Lc, 1, D // 32), np.uint16)
+    pk[0], sc[0] = 0x33, 0x3F00
+    pk[1] = 0x11
+    sc[1, ..., 0], sc[1, ..., 1] = 0x3F00, 0x4000
+    pk[2], sc[2] = 0x78, 0x4000
+    k, v = O.dequant_bank_chunks(pk, pk[::-1].copy(), sc, sc[::-1].copy(), [2, 0, 3])
+    assert k.shape == (3, Lc, 1, D) and k.dtype == np.uint16
+    assert np.all(k[0][..., 0::2] == 0xC180) and np.all(k[0][..., 1::2] == 0x4160)   # id 2
+    assert np.all(k[1] == 0x3FC0)                                                    # id 0
+    assert not k[2].any() and not v[2].any()                                         # id 3 = M
+    # v is the reversed bank: id 2 -> chunk 0's codes, id 0 -> chunk 2's codes
+    assert np.all(v[0] == 0x3FC0)
+    assert np.all(v[1][..., 0::2] == 0xC180) and np.all(v[1][..., 1::2] == 0x4160)
+    k1, _ = O.dequant_bank_chunks(pk, pk, sc, sc, [1])
+    assert np.all(k1[0][..., :32] == 0x3F00) and np.all(k1[0][..., 32:] == 0x4000)
+
+
 # ---------------------------------------------------------------- int4 encoder
 
 def _group(vals, D=32):

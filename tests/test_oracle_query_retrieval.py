@@ -95,3 +95,20 @@ def test_power_of_two_scaling_and_sign():
     assert np.array_equal(O.query_scores(km, 4.0 * qm), 4.0 * s1)
     assert np.array_equal(O.query_scores(km, -qm), -s1)
     assert np.array_equal(O.query_topk(km, 4.0 * qm, 5)[0], O.query_topk(km, qm, 5)[0])
+
+
+def test_mean_rows_out_of_range_ids_add_zero_rows_by_hand():
+    # rows 0..3 hold the values 1, 2, 4, 8 (every head and dim). The list
+    # [1, -1, 3, 4] names rows 1 and 3 and two ids outside [0, 4): those add
+    # zero rows and still count in the 1/L, so the mean is (2 + 8) / 4.
+    L_in, H, D = 4, 2, 64
+    x = np.broadcast_to(np.array([1.0, 2.0, 4.0, 8.0], np.float32)[:, None, None], (L_in, H, D))
+    m = O.mean_rows(bits(x), rows=np.array([1, -1, 3, 4]))
+    assert np.all(m == 2.5)
+    # a list of only out-of-range ids gives an all-zero mean
+    m = O.mean_rows(bits(x), rows=np.array([-5, 4, 100]))
+    assert np.all(m == 0.0)
+    # per unit: each unit's ids are checked against its own rows
+    xb = np.stack([bits(x), bits(-x)])
+    m = O.mean_rows(xb, rows=np.array([[0, 9], [-1, 2]]))
+    assert np.all(m[0] == 0.5) and np.all(m[1] == -2.0)
