@@ -151,6 +151,13 @@ int32_t wkv_keep_count(int32_t F, int32_t T, float r) {
   return (int32_t)keep_count(F, T, r);
 }
 
+int32_t wkv_compress_score_tile(int32_t B, int32_t T, int32_t H, int32_t score_mode,
+                                int32_t int4) {
+  if (B < 1 || T < 1 || H < 1) return -1;
+  if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN) return -1;
+  return wkv::compress_score_tile(B, T, H, int4 != 0 || score_mode == WKV_SCORE_ANCHOR_MEAN);
+}
+
 size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H, int32_t D,
                                     int32_t score_mode) {
   if (B < 1 || F < 2 || T < 1 || H < 1 || D < 1) return 0;
@@ -447,6 +454,30 @@ wkv_status wkv_tier_resolve(const int32_t* actual_idx, int32_t n, const int32_t*
                                           out_miss, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "wkv_tier_resolve launch");
   return WKV_OK;
+}
+
+int64_t wkv_window_rows(const wkv_segment* sink, int32_t n_ret, int32_t Lc,
+                        const wkv_segment* recent, int32_t n_recent, const wkv_segment* current) {
+  if (!sink || !current || (n_recent > 0 && !recent)) {
+    fail(WKV_ERR_NULL, "wkv_window_rows: sink, current (and recent when n_recent > 0) are required");
+    return -1;
+  }
+  if (n_ret < 0 || Lc < 0 || n_recent < 0 || n_recent > wkv::kMaxSegments - 2) {
+    fail(WKV_ERR_SHAPE, "wkv_window_rows: n_ret=%d Lc=%d n_recent=%d (0..%d)", n_ret, Lc,
+         n_recent, wkv::kMaxSegments - 2);
+    return -1;
+  }
+  int64_t rows = (int64_t)n_ret * Lc;
+  const wkv_segment* ends[2] = {sink, current};
+  for (int i = 0; i < 2 + n_recent; ++i) {
+    const wkv_segment* s = i < 2 ? ends[i] : &recent[i - 2];
+    if (s->n < 0) {
+      fail(WKV_ERR_SHAPE, "wkv_window_rows: a segment has n=%d", s->n);
+      return -1;
+    }
+    rows += s->n;
+  }
+  return rows;
 }
 
 wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,

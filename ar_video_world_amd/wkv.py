@@ -79,6 +79,7 @@ _abi_version = _sig("wkv_abi_version", _I32, [])
 _last_error = _sig("wkv_last_error", C.c_char_p, [])
 _keep_count = _sig("wkv_keep_count", _I32, [_I32, _I32, _F])
 _compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 6)
+_score_tile = _sig("wkv_compress_score_tile", _I32, [_I32] * 5)
 _compress = _sig("wkv_compress_chunk", C.c_int,
                  [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _SZ, _P])
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
@@ -108,6 +109,9 @@ _assemble = _sig("wkv_assemble_window", C.c_int,
                  [C.POINTER(wkv_segment), C.POINTER(wkv_bank), _P, _I32,
                   C.POINTER(wkv_segment), _I32, C.POINTER(wkv_segment), _I32, _I32,
                   _P, _P, _I64, _P])
+_win_rows = _sig("wkv_window_rows", _I64,
+                 [C.POINTER(wkv_segment), _I32, _I32, C.POINTER(wkv_segment), _I32,
+                  C.POINTER(wkv_segment)])
 _attn_ws = _sig("wkv_attention_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32])
 _attn = _sig("wkv_chunk_attention", C.c_int,
              [_P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P])
@@ -118,10 +122,11 @@ _attn_win = _sig("wkv_chunk_attention_window", C.c_int,
                   _P, _P, _P, _SZ, _P])
 
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
-           "wkv_compress_workspace_bytes", "wkv_compress_chunk", "wkv_compress_chunk_int4",
+           "wkv_compress_workspace_bytes", "wkv_compress_score_tile", "wkv_compress_chunk",
+           "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
            "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_pose_extrapolate", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
-           "wkv_tier_resolve",
+           "wkv_tier_resolve", "wkv_window_rows",
            "wkv_assemble_window", "wkv_attention_workspace_bytes", "wkv_chunk_attention",
            "wkv_attention_window_workspace_bytes", "wkv_chunk_attention_window"]
 
@@ -144,11 +149,71 @@ def _stream(stream) -> C.c_void_p:
 
 
 def _bits(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor, got {type(t).__name__}")
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{name}: expected bf16 (or its int16 bits), got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     return t
+
+
+def _typed(t: Optional[torch.Tensor], name: str, dtypes, shape=None, min_numel=None):
+    """Checks an argument tensor (None passes): dtype in `dtypes`, contiguous,
+    and either exactly `shape` or at least `min_numel` elements."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: expected {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+
+
+def _on_device(*named):
+    """Every tensor given (name, tensor) lives on the same GPU: the library
+    reads and writes them as device memory, so a host tensor or one on another
+    device would be an invalid device access. Raises before any launch."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: must be a CUDA (HIP) device tensor, is on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, other arguments on {dev}")
+    return dev
+
+
+def _ws_bytes(ws: Optional[torch.Tensor]) -> int:
+    if ws is None:
+        return 0
+    if not ws.is_contiguous():
+        raise ValueError("ws: must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
+def _unit_out(t, name, dtypes, shape, squeeze):
+    """An output of a batched call: exactly `shape`, or (for a call on one
+    unbatched unit) `shape` without its leading 1."""
+    if t is None:
+        return None
+    if squeeze and t.dim() == len(shape) - 1:
+        _typed(t, name, dtypes, shape[1:])
+        return t.unsqueeze(0)
+    return _typed(t, name, dtypes, shape)
 
 
 def wkv_abi_version() -> int:
@@ -178,6 +243,12 @@ def wkv_compress_workspace_bytes(B: int, F: int, T: int, H: int, D: int,
     return int(_compress_ws(B, F, T, H, D, _score_mode(score_mode)))
 
 
+def wkv_compress_score_tile(B: int, T: int, H: int, score_mode="position",
+                            int4: bool = False) -> int:
+    """Anchor tokens per block of the compression score kernel (diagnostic)."""
+    return int(_score_tile(B, T, H, _score_mode(score_mode), 1 if int4 else 0))
+
+
 def wkv_attention_workspace_bytes(Nq: int, Nk: int, H: int, D: int) -> int:
     return int(_attn_ws(Nq, Nk, H, D))
 
@@ -190,6 +261,9 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     score_mode: "position" / "anchor_mean" (or the WKV_SCORE_* value).
     Returns (k_out, v_out, kept_idx, scores-or-None)."""
     _bits(k, "k"), _bits(v, "v")
+    if k.dim() not in (3, 4) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v: expected equal [B, F*T, H, D] shapes, got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
     squeeze = k.dim() == 3
     if squeeze:
         k, v = k.unsqueeze(0), v.unsqueeze(0)
@@ -198,7 +272,13 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
         raise ValueError(f"k has {FT} rows per unit, expected F*T={F * T}")
     n_keep = wkv_keep_count(F, T, r)
     Lc = T + max(n_keep, 0)
-    dev = k.device
+    N = (F - 1) * T
+    k_out = _unit_out(k_out, "k_out", _BF16, (B, Lc, H, D), squeeze)
+    v_out = _unit_out(v_out, "v_out", _BF16, (B, Lc, H, D), squeeze)
+    kept_idx = _unit_out(kept_idx, "kept_idx", _I32, (B, Lc), squeeze)
+    scores = _unit_out(scores, "scores", (torch.float64,), (B, N), squeeze)
+    dev = _on_device(("k", k), ("v", v), ("k_out", k_out), ("v_out", v_out),
+                     ("kept_idx", kept_idx), ("scores", scores), ("ws", ws))
     if k_out is None:
         k_out = torch.empty((B, Lc, H, D), dtype=k.dtype, device=dev)
     if v_out is None:
@@ -206,13 +286,13 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     if kept_idx is None:
         kept_idx = torch.empty((B, Lc), dtype=torch.int32, device=dev)
     if scores is None and want_scores:
-        scores = torch.empty((B, (F - 1) * T), dtype=torch.float64, device=dev)
+        scores = torch.empty((B, N), dtype=torch.float64, device=dev)
     if ws is None:
         nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     st = _compress(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
                    _ptr(k_out), _ptr(v_out),
-                   _ptr(kept_idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
+                   _ptr(kept_idx), _ptr(scores), _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check("wkv_compress_chunk", st)
     if squeeze:
         k_out, v_out, kept_idx = k_out[0], v_out[0], kept_idx[0]
@@ -229,14 +309,28 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
     k_scale, v_scale, kept_idx, scores-or-None): uint8 [B, Lc, H, D/2] and
     bf16 [B, Lc, H, D/32]."""
     _bits(k, "k"), _bits(v, "v")
+    if k.dim() not in (3, 4) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v: expected equal [B, F*T, H, D] shapes, got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
     squeeze = k.dim() == 3
     if squeeze:
         k, v = k.unsqueeze(0), v.unsqueeze(0)
     B, FT, H, D = k.shape
     if FT != F * T:
         raise ValueError(f"k has {FT} rows per unit, expected F*T={F * T}")
+    if D % 32:
+        raise ValueError(f"head dim {D}: the int4 store needs a multiple of 32")
     Lc = T + max(wkv_keep_count(F, T, r), 0)
-    dev = k.device
+    N = (F - 1) * T
+    k_packed = _unit_out(k_packed, "k_packed", (torch.uint8,), (B, Lc, H, D // 2), squeeze)
+    v_packed = _unit_out(v_packed, "v_packed", (torch.uint8,), (B, Lc, H, D // 2), squeeze)
+    k_scale = _unit_out(k_scale, "k_scale", _BF16, (B, Lc, H, D // 32), squeeze)
+    v_scale = _unit_out(v_scale, "v_scale", _BF16, (B, Lc, H, D // 32), squeeze)
+    kept_idx = _unit_out(kept_idx, "kept_idx", _I32, (B, Lc), squeeze)
+    scores = _unit_out(scores, "scores", (torch.float64,), (B, N), squeeze)
+    dev = _on_device(("k", k), ("v", v), ("k_packed", k_packed), ("v_packed", v_packed),
+                     ("k_scale", k_scale), ("v_scale", v_scale), ("kept_idx", kept_idx),
+                     ("scores", scores), ("ws", ws))
     if k_packed is None:
         k_packed = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
     if v_packed is None:
@@ -248,13 +342,13 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
     if kept_idx is None:
         kept_idx = torch.empty((B, Lc), dtype=torch.int32, device=dev)
     if scores is None and want_scores:
-        scores = torch.empty((B, (F - 1) * T), dtype=torch.float64, device=dev)
+        scores = torch.empty((B, N), dtype=torch.float64, device=dev)
     if ws is None:
         nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     st = _compress4(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
                     _ptr(k_packed), _ptr(v_packed), _ptr(k_scale), _ptr(v_scale),
-                    _ptr(kept_idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
+                    _ptr(kept_idx), _ptr(scores), _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check("wkv_compress_chunk_int4", st)
     outs = [k_packed, v_packed, k_scale, v_scale, kept_idx]
     if squeeze:
@@ -302,7 +396,9 @@ def wkv_pose_topk_so3(poses: torch.Tensor, query, k: int, want_dist: bool = True
     k_eff = min(k, M)
     q = [float(t) for t in query][:7] + [0.0]
     qs = wkv_pose_q(*q)
-    dev = poses.device
+    _typed(out_idx, "out_idx", _I32, min_numel=k_eff)
+    _typed(out_dist, "out_dist", (torch.float64,), min_numel=k_eff)
+    dev = _on_device(("poses", poses), ("out_idx", out_idx), ("out_dist", out_dist))
     if out_idx is None:
         out_idx = torch.empty((max(k_eff, 1),), dtype=torch.int32, device=dev)
     if want_dist and out_dist is None:
@@ -367,13 +463,19 @@ def wkv_tier_resolve(actual_idx: torch.Tensor, slot_chunk: torch.Tensor, pred_sl
                      out_slot=None, out_miss=None, stream=None):
     """Staging slot of every retrieved chunk (stale predicted slot on a miss).
     All int32 device tensors. Returns (out_slot [n], out_miss [1])."""
-    n = int(actual_idx.shape[0])
-    dev = actual_idx.device
+    _typed(actual_idx, "actual_idx", _I32)
+    n = int(actual_idx.numel())
+    _typed(slot_chunk, "slot_chunk", _I32)
+    _typed(pred_slot, "pred_slot", _I32, min_numel=n)
+    _typed(out_slot, "out_slot", _I32, min_numel=n)
+    _typed(out_miss, "out_miss", _I32, min_numel=1)
+    dev = _on_device(("actual_idx", actual_idx), ("slot_chunk", slot_chunk),
+                     ("pred_slot", pred_slot), ("out_slot", out_slot), ("out_miss", out_miss))
     if out_slot is None:
         out_slot = torch.empty((n,), dtype=torch.int32, device=dev)
     if out_miss is None:
         out_miss = torch.empty((1,), dtype=torch.int32, device=dev)
-    st = _tier_resolve(_ptr(actual_idx), n, _ptr(slot_chunk), int(slot_chunk.shape[0]),
+    st = _tier_resolve(_ptr(actual_idx), n, _ptr(slot_chunk), int(slot_chunk.numel()),
                        _ptr(pred_slot), _ptr(out_slot), _ptr(out_miss), _stream(stream))
     _check("wkv_tier_resolve", st)
     return out_slot, out_miss
@@ -393,19 +495,24 @@ def wkv_mean_rows(x: torch.Tensor, rows=None, out=None, ws=None, stream=None):
         x = x.unsqueeze(0)
         if rows is not None:
             rows = rows.unsqueeze(0)
+    if x.dim() != 4:
+        raise ValueError(f"x: expected [B, L, H, D] or [L, H, D], got {tuple(x.shape)}")
     B, L_in, H, D = x.shape
     if rows is not None:
-        if rows.dtype != torch.int32 or not rows.is_contiguous() or rows.shape[0] != B:
+        _typed(rows, "rows", _I32)
+        if rows.dim() != 2 or rows.shape[0] != B:
             raise ValueError("rows must be a contiguous int32 [B, L] tensor")
         L = rows.shape[1]
     else:
         L = L_in
+    out = _unit_out(out, "out", (torch.float64,), (B, H, D), squeeze)
+    dev = _on_device(("x", x), ("rows", rows), ("out", out), ("ws", ws))
     if out is None:
-        out = torch.empty((B, H, D), dtype=torch.float64, device=x.device)
+        out = torch.empty((B, H, D), dtype=torch.float64, device=dev)
     if ws is None:
         ws = torch.empty(max(wkv_mean_rows_workspace_bytes(B, L, H, D), 16), dtype=torch.uint8,
-                         device=x.device)
-    st = _mean_rows(_ptr(x), B, L_in, _ptr(rows), L, H, D, _ptr(out), _ptr(ws), ws.numel(),
+                         device=dev)
+    st = _mean_rows(_ptr(x), B, L_in, _ptr(rows), L, H, D, _ptr(out), _ptr(ws), _ws_bytes(ws),
                     _stream(stream))
     _check("wkv_mean_rows", st)
     return out[0] if squeeze else out
@@ -420,10 +527,15 @@ def wkv_query_topk(key_means: torch.Tensor, query_mean: torch.Tensor, k: int, ou
         raise ValueError("key_means and query_mean must be float64")
     if not (key_means.is_contiguous() and query_mean.is_contiguous()):
         raise ValueError("key_means and query_mean must be contiguous")
+    if key_means.dim() != 3:
+        raise ValueError(f"key_means: expected [M, H, D], got {tuple(key_means.shape)}")
     M, H, D = key_means.shape
     if tuple(query_mean.shape) != (H, D):
         raise ValueError(f"query_mean shape {tuple(query_mean.shape)} != {(H, D)}")
-    dev = key_means.device
+    _typed(out_idx, "out_idx", _I32, min_numel=min(k, M))
+    _typed(scores, "scores", (torch.float64,), min_numel=M)
+    dev = _on_device(("key_means", key_means), ("query_mean", query_mean), ("out_idx", out_idx),
+                     ("scores", scores))
     if out_idx is None:
         out_idx = torch.empty((max(min(k, M), 1),), dtype=torch.int32, device=dev)
     if scores is None:
@@ -449,6 +561,7 @@ def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
     if bank_poses.dtype != torch.float32 or bank_poses.dim() != 2 or bank_poses.shape[1] != 4:
         raise TypeError("bank_poses: expected float32 [M, 4]")
     bank_poses = bank_poses.contiguous()
+    _on_device(("bank_poses", bank_poses))
     M = bank_poses.shape[0]
     hist = list(query_hist)
     if len(hist) == 4 and not hasattr(hist[0], "__len__"):
@@ -460,10 +573,8 @@ def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
     if out_idx is None:
         idx = torch.empty(max(k_eff, 1), dtype=torch.int32, device=dev)
     else:
-        if (out_idx.dtype != torch.int32 or not out_idx.is_contiguous()
-                or out_idx.numel() < k_eff or out_idx.device != dev):
-            raise TypeError("out_idx: expected a contiguous int32 tensor of >= k_eff elements "
-                            "on the bank's device")
+        _typed(out_idx, "out_idx", _I32, min_numel=k_eff)
+        _on_device(("bank_poses", bank_poses), ("out_idx", out_idx))
         idx = out_idx[:k_eff]
     dist = torch.empty(max(k_eff, 1), dtype=torch.float64, device=dev) if want_dist else None
     q = torch.empty(4, dtype=torch.float32, device=dev) if want_query else None
@@ -473,12 +584,56 @@ def wkv_pose_topk(bank_poses: torch.Tensor, query_hist: Sequence, k: int,
     return idx, dist, q
 
 
-def _seg(pair) -> wkv_segment:
+def _seg(pair, H: Optional[int] = None, D: Optional[int] = None, name: str = "segment",
+         named: Optional[list] = None) -> wkv_segment:
+    """A (k, v) pair of bf16 [n, H, D] rows as a wkv_segment; k and v must
+    have the same shape, with trailing (H, D) when given. The tensors are
+    appended to `named` for the device check."""
     if pair is None:
         return wkv_segment(None, None, 0)
     k, v = pair
-    _bits(k, "segment k"), _bits(v, "segment v")
+    _bits(k, f"{name} k"), _bits(v, f"{name} v")
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"{name}: k, v must be equal [n, H, D] shapes, got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    if H is not None and tuple(k.shape[1:]) != (int(H), int(D)):
+        raise ValueError(f"{name}: rows of {tuple(k.shape[1:])}, expected (H, D) = {(H, D)}")
+    if named is not None:
+        named += [(f"{name} k", k), (f"{name} v", v)]
     return wkv_segment(k.data_ptr(), v.data_ptr(), int(k.shape[0]))
+
+
+def _bank_arg(bank, n_ret: int, H: int, D: int, named: list) -> wkv_bank:
+    """The bank dict as a wkv_bank: bf16 [M, Lc, H, D] k / v, or the int4 store
+    (uint8 [M, Lc, H, D/2] k / v with bf16 [M, Lc, H, D/32] scales)."""
+    bk = wkv_bank(0, 0, 0, None, None, None, None)
+    if bank is None or n_ret == 0:
+        return bk
+    int4 = bank.get("k_scale") is not None
+    k, v = bank["k"], bank["v"]
+    if int4:
+        _typed(k, "bank k", (torch.uint8,))
+        _typed(v, "bank v", (torch.uint8,), tuple(k.shape))
+        if k.dim() != 4 or tuple(k.shape[2:]) != (H, D // 2):
+            raise ValueError(f"bank k: int4 store of shape {tuple(k.shape)}, expected "
+                             f"[M, Lc, {H}, {D // 2}]")
+        sshape = tuple(k.shape[:2]) + (H, D // 32)
+        _typed(bank["k_scale"], "bank k_scale", _BF16, sshape)
+        _typed(bank["v_scale"], "bank v_scale", _BF16, sshape)
+        named += [("bank k", k), ("bank v", v), ("bank k_scale", bank["k_scale"]),
+                  ("bank v_scale", bank["v_scale"])]
+    else:
+        _bits(k, "bank k"), _bits(v, "bank v")
+        if k.dim() != 4 or tuple(v.shape) != tuple(k.shape) or tuple(k.shape[2:]) != (H, D):
+            raise ValueError(f"bank k, v: shapes {tuple(k.shape)}, {tuple(v.shape)}, expected "
+                             f"equal [M, Lc, {H}, {D}]")
+        named += [("bank k", k), ("bank v", v)]
+    bk.dtype = WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16
+    bk.M, bk.Lc = int(k.shape[0]), int(k.shape[1])
+    bk.k, bk.v = k.data_ptr(), v.data_ptr()
+    if int4:
+        bk.k_scale, bk.v_scale = bank["k_scale"].data_ptr(), bank["v_scale"].data_ptr()
+    return bk
 
 
 def wkv_assemble_window(sink, bank, retrieved_idx: Optional[torch.Tensor], recent, current,
@@ -488,27 +643,38 @@ def wkv_assemble_window(sink, bank, retrieved_idx: Optional[torch.Tensor], recen
     sink, current: (k, v) bf16 [n, H, D]. recent: list of (k, v).
     bank: dict with 'k', 'v' (bf16 [M, Lc, H, D], or uint8 [M, Lc, H, D/2] with
     'k_scale', 'v_scale' bf16 [M, Lc, H, D/32] for the int4 store), or None.
+    retrieved_idx: int32 device tensor of chunk ids (e.g. from wkv_pose_topk).
+    win_k / win_v: optional outputs of at least Nk rows of (H, D).
     Returns (win_k, win_v)."""
-    sk = _seg(sink)
-    cur = _seg(current)
+    named = []
+    sk = _seg(sink, H, D, "sink", named)
+    cur = _seg(current, H, D, "current", named)
     rec_list = list(recent or [])
-    rec = (wkv_segment * max(len(rec_list), 1))(*[_seg(p) for p in rec_list])
+    rec = (wkv_segment * max(len(rec_list), 1))(
+        *[_seg(p, H, D, f"recent[{i}]", named) for i, p in enumerate(rec_list)])
+    _typed(retrieved_idx, "retrieved_idx", _I32)
     n_ret = 0 if retrieved_idx is None else int(retrieved_idx.numel())
-    bk = wkv_bank(0, 0, 0, None, None, None, None)
-    if bank is not None and n_ret > 0:
-        int4 = "k_scale" in bank and bank["k_scale"] is not None
-        bk.dtype = WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16
-        bk.M, bk.Lc = int(bank["k"].shape[0]), int(bank["k"].shape[1])
-        bk.k, bk.v = bank["k"].data_ptr(), bank["v"].data_ptr()
-        if int4:
-            bk.k_scale, bk.v_scale = bank["k_scale"].data_ptr(), bank["v_scale"].data_ptr()
+    bk = _bank_arg(bank, n_ret, H, D, named)
     Lc = bk.Lc if n_ret > 0 else 0
-    Nk = sk.n + n_ret * Lc + sum(int(p[0].shape[0]) for p in rec_list) + cur.n
-    dev = (sink[0] if sink is not None else current[0]).device
+    Nk = int(_win_rows(C.byref(sk), n_ret, Lc, rec, len(rec_list), C.byref(cur)))
+    if Nk < 0:
+        raise ValueError(f"wkv_assemble_window: {wkv_last_error()}")
+    for name, t in (("win_k", win_k), ("win_v", win_v)):
+        if t is not None:
+            _bits(t, name)
+            if t.dim() != 3 or tuple(t.shape[1:]) != (H, D) or t.shape[0] < Nk:
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, expected at least "
+                                 f"({Nk}, {H}, {D})")
+    if win_k is not None and win_v is not None and win_k.shape[0] != win_v.shape[0]:
+        raise ValueError("win_k and win_v must have the same number of rows")
+    dev = _on_device(*named, ("retrieved_idx", retrieved_idx), ("win_k", win_k),
+                     ("win_v", win_v))
+    if dev is None:
+        raise ValueError("wkv_assemble_window: no device tensor given")
     if win_k is None:
         win_k = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev)
     if win_v is None:
-        win_v = torch.empty((Nk, H, D), dtype=torch.bfloat16, device=dev)
+        win_v = torch.empty((win_k.shape[0], H, D), dtype=torch.bfloat16, device=dev)
     st = _assemble(C.byref(sk), C.byref(bk), _ptr(retrieved_idx), n_ret, rec, len(rec_list),
                    C.byref(cur), H, D, _ptr(win_k), _ptr(win_v), int(win_k.shape[0]),
                    _stream(stream))
@@ -522,9 +688,16 @@ def wkv_chunk_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Unmasked attention of q [Nq, H, D] over k, v [Nk, H, D] (bf16).
     Returns (out bf16 [Nq, H, D], lse float32 [H, Nq] or None)."""
     _bits(q, "q"), _bits(k, "k"), _bits(v, "v")
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [Nq, H, D], got {tuple(q.shape)}")
     Nq, H, D = q.shape
+    if k.dim() != 3 or tuple(k.shape[1:]) != (H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v: expected equal [Nk, {H}, {D}] shapes, got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
     Nk = k.shape[0]
-    dev = q.device
+    _typed(out, "out", _BF16, (Nq, H, D))
+    _typed(lse, "lse", (torch.float32,), (H, Nq))
+    dev = _on_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("ws", ws))
     if out is None:
         out = torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
@@ -533,7 +706,7 @@ def wkv_chunk_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nb = wkv_attention_workspace_bytes(Nq, Nk, H, D)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     st = _attn(_ptr(q), _ptr(k), _ptr(v), Nq, Nk, H, D, float(scale), _ptr(out), _ptr(lse),
-               _ptr(ws), ws.numel(), _stream(stream))
+               _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check("wkv_chunk_attention", st)
     return out, lse
 
@@ -552,22 +725,25 @@ def wkv_chunk_attention_window(q: torch.Tensor, sink, bank, retrieved_idx: Optio
     wkv_assemble_window (bf16 bank only) and wkv_chunk_attention.
     Returns (out bf16 [Nq, H, D], lse float32 [H, Nq] or None)."""
     _bits(q, "q")
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [Nq, H, D], got {tuple(q.shape)}")
     Nq, H, D = q.shape
-    sk = _seg(sink)
-    cur = _seg(current)
+    named = [("q", q)]
+    sk = _seg(sink, H, D, "sink", named)
+    cur = _seg(current, H, D, "current", named)
     rec_list = list(recent or [])
-    rec = (wkv_segment * max(len(rec_list), 1))(*[_seg(p) for p in rec_list])
+    rec = (wkv_segment * max(len(rec_list), 1))(
+        *[_seg(p, H, D, f"recent[{i}]", named) for i, p in enumerate(rec_list)])
+    _typed(retrieved_idx, "retrieved_idx", _I32)
     n_ret = 0 if retrieved_idx is None else int(retrieved_idx.numel())
-    bk = wkv_bank(0, 0, 0, None, None, None, None)
-    if bank is not None and n_ret > 0:
-        int4 = "k_scale" in bank and bank["k_scale"] is not None
-        bk.dtype = WKV_BANK_INT4_G32 if int4 else WKV_BANK_BF16
-        bk.M, bk.Lc = int(bank["k"].shape[0]), int(bank["k"].shape[1])
-        bk.k, bk.v = bank["k"].data_ptr(), bank["v"].data_ptr()
+    bk = _bank_arg(bank, n_ret, H, D, named)
     Lc = bk.Lc if n_ret > 0 else 0
     lens = [sk.n] + [Lc] * n_ret + [int(p[0].shape[0]) for p in rec_list] + [cur.n]
     nk_pad = sum(64 * ((n + 63) // 64) for n in lens)
-    dev = q.device
+    _typed(out, "out", _BF16, (Nq, H, D))
+    _typed(lse, "lse", (torch.float32,), (H, Nq))
+    dev = _on_device(*named, ("retrieved_idx", retrieved_idx), ("out", out), ("lse", lse),
+                     ("ws", ws))
     if out is None:
         out = torch.empty((Nq, H, D), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
@@ -577,6 +753,6 @@ def wkv_chunk_attention_window(q: torch.Tensor, sink, bank, retrieved_idx: Optio
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
     st = _attn_win(_ptr(q), Nq, C.byref(sk), C.byref(bk), _ptr(retrieved_idx), n_ret, rec,
                    len(rec_list), C.byref(cur), H, D, float(scale), _ptr(out), _ptr(lse),
-                   _ptr(ws), ws.numel(), _stream(stream))
+                   _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check("wkv_chunk_attention_window", st)
     return out, lse

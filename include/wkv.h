@@ -141,6 +141,16 @@ enum { WKV_SCORE_POSITION = 0, WKV_SCORE_ANCHOR_MEAN = 1 };
 size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H,
                                     int32_t D, int32_t score_mode);
 
+/* [host] Diagnostic: anchor-frame tokens each block of the compression score
+ * kernel covers for a call on B units of T tokens and H heads with the given
+ * score mode, int4 != 0 for wkv_compress_chunk_int4. The tile starts at one
+ * pass of (token, head) pairs and, where each block carries fixed work that
+ * more tokens amortise (the int4 store, the anchor-mean score), doubles while
+ * the grid keeps >= 2048 blocks. It changes no result; tests use it to reach
+ * every tile size. -1 for invalid arguments. */
+int32_t wkv_compress_score_tile(int32_t B, int32_t T, int32_t H, int32_t score_mode,
+                                int32_t int4);
+
 /* Compress B contiguous units.
  *   k, v       bf16 [B][F*T][H][D]            inputs
  *   k_out,
@@ -196,8 +206,8 @@ wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t
  * The query pose: n_hist = 1 -> query_hist[0]; n_hist = 2 -> extrapolated
  * linearly from query_hist[0] (previous) and query_hist[1] (last):
  * q = last + (last - prev), yaw = wrap(yaw_l + wrap(yaw_l - yaw_p)), formed
- * in float64 and stored as float ([WorldPager] Fig. 2: the retrieval set of
- * the next chunk comes from the extrapolated pose).
+ * in float64 and stored as float ([WorldPager] Fig. 2: prefetch for the
+ * next chunk is driven by a linearly extrapolated pose).
  *   bank_poses  wkv_pose [M]          device, 1 <= M <= 8192
  *   query_hist  wkv_pose [n_hist]     [host]
  *   out_idx     int32 [k_eff]         output, ascending chunk ids
@@ -210,7 +220,7 @@ wkv_status wkv_pose_topk(const wkv_pose* bank_poses, int32_t M,
                          wkv_pose* out_query, wkv_stream_t stream);
 
 /* [host] The query pose extrapolated one chunk ahead ([WorldPager] Fig. 2:
- * the next retrieval set comes from the extrapolated camera pose):
+ * next-chunk retrieval runs on a linearly extrapolated pose):
  * translation last + (last - prev), yaw wrap(yaw_l + wrap(yaw_l - yaw_p)),
  * in float64, rounded to float. wkv_pose_topk with n_hist = 2 uses it. */
 wkv_pose wkv_pose_extrapolate(wkv_pose prev, wkv_pose last);
@@ -372,6 +382,13 @@ wkv_status wkv_tier_resolve(const int32_t* actual_idx, int32_t n, const int32_t*
  *   retrieved_idx  int32 [n_ret] device (e.g. out_idx of wkv_pose_topk)
  *   recent         [host] wkv_segment [n_recent], 0 <= n_recent <= 14
  * ------------------------------------------------------------------------ */
+/* [host] Rows of the window wkv_assemble_window writes for these pieces:
+ * sink->n + n_ret * Lc + sum(recent[i].n) + current->n (the caller sizes
+ * win_k / win_v with it). -1 for a NULL piece, a negative count or more than
+ * 14 recent segments (the reason is in wkv_last_error()). */
+int64_t wkv_window_rows(const wkv_segment* sink, int32_t n_ret, int32_t Lc,
+                        const wkv_segment* recent, int32_t n_recent, const wkv_segment* current);
+
 wkv_status wkv_assemble_window(const wkv_segment* sink, const wkv_bank* bank,
                                const int32_t* retrieved_idx, int32_t n_ret,
                                const wkv_segment* recent, int32_t n_recent,
