@@ -70,3 +70,22 @@ def check_attention(o_gpu: torch.Tensor, o_ref: np.ndarray):
     assert stats["max_abs"] <= ATT_MAX_ABS, stats
     assert stats["mean_abs"] <= ATT_MEAN_ABS, stats
     return stats
+
+
+def guarded(shape, dtype, device, guard: int = 4096, sentinel: int = 0x5A):
+    """An output tensor of `shape` that is the head of a larger buffer whose
+    tail (`guard` elements past the end) holds a sentinel byte pattern.
+    Returns (view, tail); check_guard(tail, ...) proves nothing was written
+    past the output's end."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    esz = torch.empty((), dtype=dtype).element_size()
+    raw = torch.full(((n + guard) * esz,), sentinel, dtype=torch.uint8, device=device)
+    full = raw.view(dtype)
+    return full[:n].view(shape), full[n:]
+
+
+def check_guard(tail: torch.Tensor, label: str, sentinel: int = 0x5A):
+    b = tail.contiguous().view(torch.uint8).cpu().numpy()
+    assert np.all(b == sentinel), f"{label}: output written past its end ({int(np.sum(b != sentinel))} bytes)"

@@ -11,7 +11,7 @@ import torch
 
 import wkv_synth as S
 from oracle import wkv_oracle as O
-from tests.parity import check_attention, gpu_ready, np_bits, say
+from tests.parity import check_attention, check_guard, gpu_ready, guarded, np_bits, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs the built library and a GPU")]
@@ -43,8 +43,13 @@ def attn_case(w, Nq, Nk, H, D, label, sample=None, small_ws=False, cfg=21):
     q, k, v = qkv(cfg, Nq, Nk, H, D)
     say("attention", label, "Nq", Nq, "Nk", Nk, "H", H, "D", D, "small_ws", small_ws)
     ws = torch.empty(16, dtype=torch.uint8, device=DEV) if small_ws else None
-    o, lse = w.wkv_chunk_attention(q, k, v, want_lse=True, ws=ws)
+    # outputs are the heads of buffers whose sentinel tails must survive
+    out, tout = guarded((Nq, H, D), torch.bfloat16, DEV)
+    lse, tlse = guarded((H, Nq), torch.float32, DEV)
+    o, lse = w.wkv_chunk_attention(q, k, v, out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
+    check_guard(tout, f"{label} out")
+    check_guard(tlse, f"{label} lse")
     rows = np.arange(Nq) if sample is None else np.asarray(sample)
     qb = np_bits(q)[rows]
     ro, rl = O.chunk_attention(qb, np_bits(k), np_bits(v))
@@ -117,6 +122,22 @@ def test_14b_full_size_sampled(w):
     Nq, Nk, H, D = 4680, 32760, 40, 128
     sample = list(range(0, 24)) + list(range(4600, 4680))
     attn_case(w, Nq, Nk, H, D, "14B r=0.25", sample=sample)
+
+
+def test_13b_alt_ratio_full_size_sampled(w):
+    # 1.3B-class window at the alternative keep ratio r = 0.25: 3 retrieved
+    # chunks of 1320 rows, 14,520 keys
+    Nq, Nk, H, D = 2640, 14520, 12, 128
+    sample = list(range(0, 40)) + list(range(2580, 2640))
+    attn_case(w, Nq, Nk, H, D, "1.3B r=0.25", sample=sample)
+
+
+def test_14b_alt_ratio_full_size_sampled(w):
+    # 14B-class window at the alternative keep ratio r = 0.5: 6 retrieved
+    # chunks of 3120 rows, 37,440 keys
+    Nq, Nk, H, D = 4680, 37440, 40, 128
+    sample = list(range(0, 16)) + list(range(4620, 4680))
+    attn_case(w, Nq, Nk, H, D, "14B r=0.5", sample=sample)
 
 
 def test_deterministic(w):

@@ -76,3 +76,87 @@ def test_chain_13b(w, score_mode):
     print(f"  chain {score_mode}: attention max-abs {err.max():.3e} mean-abs {err.mean():.3e}",
           flush=True)
     assert err.max() <= ATT_MAX_ABS and err.mean() <= ATT_MEAN_ABS
+
+
+def test_chain_int4_long_rollout(w):
+    """The long-rollout int4 store (WorldPager abstract and Fig. 2: int4 KV
+    written at eviction, next-chunk retrieval from a linearly extrapolated
+    pose): a 1000-chunk bank of the 1.3B-class shape compressed at r = 0.5 by
+    wkv_compress_chunk_int4 (batches of 100 units), top-4 by the pose
+    extrapolated from the last two, int4 assembly of sink | 4 retrieved |
+    2 recent | current (17,600 keys) and attention over it. Checked against
+    the oracle: the retrieved chunks and 6 spread ones of the bank (each
+    regenerated and compressed by the oracle), the retrieval, the whole
+    window bitwise, and the attention on sampled rows."""
+    F, T, H, D, r, M, k = 3, 880, 12, 128, 0.5, 1000, 4
+    FT = F * T
+    n_keep = O.keep_count(F, T, r)
+    Lc = T + n_keep
+    kp = torch.empty((M, Lc, H, D // 2), dtype=torch.uint8, device=DEV)
+    vp = torch.empty_like(kp)
+    ks = torch.empty((M, Lc, H, D // 32), dtype=torch.bfloat16, device=DEV)
+    vs = torch.empty_like(ks)
+    ki = torch.empty((M, Lc), dtype=torch.int32, device=DEV)
+    nb = 100
+    kin = torch.empty((nb, FT, H, D), dtype=torch.bfloat16, device=DEV)
+    vin = torch.empty_like(kin)
+    for b0 in range(0, M, nb):
+        for u in range(nb):
+            kin[u], vin[u] = S.chunk_kv(5, 3000 + b0 + u, 0, F, T, H, D, device=DEV)
+        say("chain int4", "compress units", b0, b0 + nb)
+        w.wkv_compress_chunk_int4(kin, vin, F, T, r, k_packed=kp[b0:b0 + nb],
+                                  v_packed=vp[b0:b0 + nb], k_scale=ks[b0:b0 + nb],
+                                  v_scale=vs[b0:b0 + nb], kept_idx=ki[b0:b0 + nb])
+    torch.cuda.synchronize()
+    del kin, vin
+
+    walk = S.pose_walk(5, M + 3)
+    poses = walk[1:M + 1].contiguous()
+    hist = [walk[M + 1].tolist(), walk[M + 2].tolist()]
+    say("chain int4", "retrieve (extrapolated pose)")
+    idx, dist, qpose = w.wkv_pose_topk(poses.to(DEV), hist, k, want_query=True)
+    qo = O.pose_extrapolate(np.asarray(hist[0], np.float32), np.asarray(hist[1], np.float32))
+    oidx, odist = O.pose_topk(poses.numpy(), qo, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(qpose.cpu().numpy(), qo)
+    assert np.array_equal(idx.cpu().numpy(), oidx) and np.array_equal(dist.cpu().numpy(), odist)
+
+    # bank entries against the oracle's compression of the same chunks
+    check = sorted(set(int(i) for i in oidx) | {0, 199, 400, 601, 802, M - 1})
+    for m in check:
+        kc, vc = S.chunk_kv(5, 3000 + m, 0, F, T, H, D, device=DEV)
+        say("chain int4", "oracle unit", m)
+        okp, ovp, oks, ovs, oi, osc = O.compress_chunk_int4(np_bits(kc), np_bits(vc), F, T, r)
+        gki = ki[m].cpu().numpy()
+        _, ndiff = check_selection(oi, gki, osc, T, n_keep)
+        if ndiff == 0:
+            assert np.array_equal(gki, oi)
+            assert np.array_equal(kp[m].cpu().numpy(), okp) and np.array_equal(np_bits(ks[m]), oks)
+            assert np.array_equal(vp[m].cpu().numpy(), ovp) and np.array_equal(np_bits(vs[m]), ovs)
+
+    segs = [S.segment_kv(5, 900 + j, FT, H, D) for j in range(4)]
+    sink, rec, cur = segs[0], segs[1:3], segs[3]
+    d = lambda p: (p[0].to(DEV), p[1].to(DEV))
+    b = lambda p: (np_bits(p[0]), np_bits(p[1]))
+    say("chain int4", "assemble")
+    bank = {"k": kp, "v": vp, "k_scale": ks, "v_scale": vs}
+    wk, wv = w.wkv_assemble_window(d(sink), bank, idx, [d(x) for x in rec], d(cur), H, D)
+    assert wk.shape[0] == 17600
+    # the oracle dequantises the GPU bank's retrieved chunks (only those leave the device)
+    sel = torch.as_tensor(oidx.astype(np.int64), device=DEV)
+    obank = O.dequant_bank_chunks(kp[sel].cpu().numpy(), vp[sel].cpu().numpy(),
+                                  np_bits(ks[sel]), np_bits(vs[sel]), range(k))
+    owk, owv = O.assemble_window(b(sink), obank, range(k), [b(x) for x in rec], b(cur))
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(wk), owk) and np.array_equal(np_bits(wv), owv)
+
+    qs = S.queries(5, 0, FT, H, D)
+    say("chain int4", "attention")
+    out, _ = w.wkv_chunk_attention(qs.to(DEV), wk, wv)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 128), np.arange(FT - 80, FT)])
+    oo, _ = O.chunk_attention(np_bits(qs)[rows], owk, owv)
+    got = O.bf16_to_f64(np_bits(out)[rows])
+    err = np.abs(got - oo)
+    print(f"  chain int4: attention max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
+    assert err.max() <= ATT_MAX_ABS and err.mean() <= ATT_MEAN_ABS

@@ -10,7 +10,7 @@ import torch
 
 import wkv_synth as S
 from oracle import wkv_oracle as O
-from tests.parity import check_selection, gpu_ready, np_bits, say
+from tests.parity import check_guard, check_selection, gpu_ready, guarded, np_bits, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs the built library and a GPU")]
@@ -22,37 +22,48 @@ def w():
     return w
 
 
-def run_case(w, K, V, F, T, r, label, want_scores=True, report=None, score_mode="position"):
-    """K, V: CPU bf16 [B, F*T, H, D]. Compares every unit with the oracle."""
-    B = K.shape[0]
+def run_case(w, K, V, F, T, r, label, want_scores=True, report=None, score_mode="position",
+             units=None):
+    """K, V: bf16 [B, F*T, H, D] (host or device). Compares the listed units
+    (default: every unit) with the oracle."""
+    B, _, H, D = K.shape
     dev = torch.device("cuda:0")
     say("compress", label, tuple(K.shape), "r", r, score_mode)
-    ko, vo, ki, sc = w.wkv_compress_chunk(K.to(dev), V.to(dev), F, T, r,
-                                          want_scores=want_scores, score_mode=score_mode)
+    Lc = T + O.keep_count(F, T, r)
+    # every output is the head of a buffer whose sentinel tail must survive
+    ko, tko = guarded((B, Lc, H, D), torch.bfloat16, dev)
+    vo, tvo = guarded((B, Lc, H, D), torch.bfloat16, dev)
+    ki, tki = guarded((B, Lc), torch.int32, dev)
+    sc, tsc = guarded((B, (F - 1) * T), torch.float64, dev) if want_scores else (None, None)
+    ko, vo, ki, sc = w.wkv_compress_chunk(K.to(dev), V.to(dev), F, T, r, k_out=ko, v_out=vo,
+                                          kept_idx=ki, scores=sc, score_mode=score_mode)
     torch.cuda.synchronize()
-    ko, vo, ki = np_bits(ko), np_bits(vo), ki.cpu().numpy()
-    sc = sc.cpu().numpy() if sc is not None else None
+    for t, n in ((tko, "k_out"), (tvo, "v_out"), (tki, "kept_idx"), (tsc, "scores")):
+        if t is not None:
+            check_guard(t, f"{label} {n}")
     n_keep = O.keep_count(F, T, r)
     bands = []
-    for b in range(B):
+    for b in (range(B) if units is None else units):
         kb, vb = np_bits(K[b]), np_bits(V[b])
         ok, ov, oi, os_ = O.compress_chunk(kb, vb, F, T, r, score_mode=score_mode)
+        gko, gvo, gki = np_bits(ko[b]), np_bits(vo[b]), ki[b].cpu().numpy()
         if sc is not None:
-            both_nan = np.isnan(os_) & np.isnan(sc[b])
-            d = np.where(both_nan, 0.0, np.abs(sc[b] - os_))
+            gsc = sc[b].cpu().numpy()
+            both_nan = np.isnan(os_) & np.isnan(gsc)
+            d = np.where(both_nan, 0.0, np.abs(gsc - os_))
             assert np.nanmax(d) <= 1e-12, f"{label} unit {b}: score error {np.nanmax(d)}"
-        nb, ndiff = check_selection(oi, ki[b], os_, T, n_keep)
+        nb, ndiff = check_selection(oi, gki, os_, T, n_keep)
         bands.append((nb, ndiff))
-        assert ki[b].shape[0] == T + n_keep
-        assert np.array_equal(ki[b][:T], np.arange(T))
-        assert np.all(np.diff(ki[b]) > 0)
+        assert gki.shape[0] == T + n_keep
+        assert np.array_equal(gki[:T], np.arange(T))
+        assert np.all(np.diff(gki) > 0)
         if ndiff == 0:
-            assert np.array_equal(ki[b], oi), label
-            assert np.array_equal(ko[b], ok), label
-            assert np.array_equal(vo[b], ov), label
+            assert np.array_equal(gki, oi), label
+            assert np.array_equal(gko, ok), label
+            assert np.array_equal(gvo, ov), label
         else:
-            for i, src in enumerate(ki[b]):
-                assert np.array_equal(ko[b][i], kb[src]) and np.array_equal(vo[b][i], vb[src])
+            for i, src in enumerate(gki):
+                assert np.array_equal(gko[i], kb[src]) and np.array_equal(gvo[i], vb[src])
     if report is not None:
         report[label] = bands
     print(f"  {label}: band sizes / differing {bands}", flush=True)

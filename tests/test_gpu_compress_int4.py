@@ -12,7 +12,7 @@ import torch
 
 import wkv_synth as S
 from oracle import wkv_oracle as O
-from tests.parity import check_selection, gpu_ready, np_bits, say
+from tests.parity import check_guard, check_selection, gpu_ready, guarded, np_bits, say
 from tests.test_gpu_compress import gen_units
 
 pytestmark = [pytest.mark.gpu,
@@ -25,38 +25,54 @@ def w():
     return w
 
 
-def run_int4(w, K, V, F, T, r, label, score_mode="position", want_scores=True):
-    B = K.shape[0]
+def run_int4(w, K, V, F, T, r, label, score_mode="position", want_scores=True, units=None):
+    """K, V: bf16 [B, F*T, H, D] (host or device). units: the units compared
+    with the oracle (default: all)."""
+    B, _, H, D = K.shape
     dev = torch.device("cuda:0")
     say("compress_int4", label, tuple(K.shape), "r", r, score_mode)
+    Lc = T + O.keep_count(F, T, r)
+    # every output is the head of a buffer whose sentinel tail must survive
+    kp, tkp = guarded((B, Lc, H, D // 2), torch.uint8, dev)
+    vp, tvp = guarded((B, Lc, H, D // 2), torch.uint8, dev)
+    ks, tks = guarded((B, Lc, H, D // 32), torch.bfloat16, dev)
+    vs, tvs = guarded((B, Lc, H, D // 32), torch.bfloat16, dev)
+    ki, tki = guarded((B, Lc), torch.int32, dev)
+    sc, tsc = guarded((B, (F - 1) * T), torch.float64, dev) if want_scores else (None, None)
     kp, vp, ks, vs, ki, sc = w.wkv_compress_chunk_int4(K.to(dev), V.to(dev), F, T, r,
-                                                       want_scores=want_scores,
+                                                       k_packed=kp, v_packed=vp, k_scale=ks,
+                                                       v_scale=vs, kept_idx=ki, scores=sc,
                                                        score_mode=score_mode)
     torch.cuda.synchronize()
-    kp, vp = kp.cpu().numpy(), vp.cpu().numpy()
-    ks, vs, ki = np_bits(ks), np_bits(vs), ki.cpu().numpy()
+    for t, n in ((tkp, "k_packed"), (tvp, "v_packed"), (tks, "k_scale"), (tvs, "v_scale"),
+                 (tki, "kept_idx"), (tsc, "scores")):
+        if t is not None:
+            check_guard(t, f"{label} {n}")
     n_keep = O.keep_count(F, T, r)
     bands = []
-    for b in range(B):
+    for b in (range(B) if units is None else units):
         kb, vb = np_bits(K[b]), np_bits(V[b])
         okp, ovp, oks, ovs, oi, osc = O.compress_chunk_int4(kb, vb, F, T, r, score_mode)
+        gkp, gvp = kp[b].cpu().numpy(), vp[b].cpu().numpy()
+        gks, gvs, gki = np_bits(ks[b]), np_bits(vs[b]), ki[b].cpu().numpy()
         if sc is not None:
             d = np.abs(sc[b].cpu().numpy() - osc)
             assert np.nanmax(d) <= 1e-12, f"{label}: score error {np.nanmax(d)}"
-        nb, ndiff = check_selection(oi, ki[b], osc, T, n_keep)
+        nb, ndiff = check_selection(oi, gki, osc, T, n_keep)
         bands.append((nb, ndiff))
         if ndiff == 0:
-            assert np.array_equal(ki[b], oi)
-            for got, exp, what in ((kp[b], okp, "k codes"), (vp[b], ovp, "v codes"),
-                                   (ks[b], oks, "k scales"), (vs[b], ovs, "v scales")):
+            assert np.array_equal(gki, oi)
+            for got, exp, what in ((gkp, okp, "k codes"), (gvp, ovp, "v codes"),
+                                   (gks, oks, "k scales"), (gvs, ovs, "v scales")):
                 bad = np.argwhere(got != exp)
                 assert bad.size == 0, f"{label} unit {b}: {what} differ at {bad[:5].tolist()}"
         else:
-            rk, rks = O.int4_quantize(kb[ki[b]])
-            rv, rvs = O.int4_quantize(vb[ki[b]])
-            assert np.array_equal(kp[b], rk) and np.array_equal(ks[b], rks)
-            assert np.array_equal(vp[b], rv) and np.array_equal(vs[b], rvs)
+            rk, rks = O.int4_quantize(kb[gki])
+            rv, rvs = O.int4_quantize(vb[gki])
+            assert np.array_equal(gkp, rk) and np.array_equal(gks, rks)
+            assert np.array_equal(gvp, rv) and np.array_equal(gvs, rvs)
     print(f"  {label}: band sizes / differing {bands}", flush=True)
+    return bands
 
 
 @pytest.mark.parametrize("r", [0.0, 0.25, 0.5, 1.0])
