@@ -13,7 +13,13 @@ several input sets rotate so the bandwidth-bound calls are not served from the
 last-level cache. After the timed region the CPU oracle runs on a bounded
 sample of the same workload (reported as ``cpu_baseline``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1.3b]
+The default workload is the 14B-class single layer (40 heads x d128, 3x1560-token
+chunks, 4 denoising steps), the largest that fits one GPU; the 1.3B-class, tiny
+and int4-store configurations and the compression sweep are selected with
+--config. The breakdown also times batched compression of 300 units of the
+1.3B-class chunk shape (bf16 and int4 stores, r = 0.25 and 0.5).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 14b]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -69,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="1.3b", choices=sorted(CONFIGS) + ["sweep"])
+    ap.add_argument("--config", default="14b", choices=sorted(CONFIGS) + ["sweep"])
     ap.add_argument("--r", type=float, default=None, help="override the keep ratio")
     ap.add_argument("--score-mode", default="position", choices=["position", "anchor_mean"],
                     help="compression score: cosine to the anchor key at the same position "
@@ -87,6 +93,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate oracle work in the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batches", action="store_true",
+                    help="skip the batched 300-unit compression cells of the breakdown")
+    ap.add_argument("--sample-units", type=int, default=30,
+                    help="units per sweep cell checked against the oracle (CPU baseline leg)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -487,6 +497,9 @@ def main():
             copy_gbps = 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
             del src, dst
 
+    # batched compression of 300 units beside the step (timed cells)
+    batches = None if a.no_batches else compress_batches(a, torch, w, S, dev)
+
     ms_per_step = wall / a.steps * 1e3
     comp_b, asm_b = algorithmic_bytes(c, Lc, n_keep, Nk)
     flops = 4.0 * Nq * Nk * D * H
@@ -547,6 +560,7 @@ def main():
                                                ("assemble", t_asm), ("attention", t_att))},
             "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
             "window_in_place": inplace,
+            "compress_batches": batches,
         },
         "roofline": {
             "kernel": "wkv_chunk_attention" + (" (fwd + split merge)" if splits else ""),
@@ -565,16 +579,105 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def _compress_outputs(torch, B, Lc, H, D, store, dev):
+    """Output buffers of one batched compression call."""
+    ki = torch.empty((B, Lc), dtype=torch.int32, device=dev)
+    if store == "int4":
+        ko = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B, Lc, H, D // 32), dtype=torch.bfloat16, device=dev)
+        return dict(kp=ko, vp=torch.empty_like(ko), ks=ks, vs=torch.empty_like(ks), ki=ki)
+    ko = torch.empty((B, Lc, H, D), dtype=torch.bfloat16, device=dev)
+    return dict(ko=ko, vo=torch.empty_like(ko), ki=ki)
+
+
+def _compress_call(w, kin, vin, F, T, r, out, ws, score_mode):
+    if "kp" in out:
+        w.wkv_compress_chunk_int4(kin, vin, F, T, r, k_packed=out["kp"], v_packed=out["vp"],
+                                  k_scale=out["ks"], v_scale=out["vs"], kept_idx=out["ki"],
+                                  ws=ws, score_mode=score_mode)
+    else:
+        w.wkv_compress_chunk(kin, vin, F, T, r, k_out=out["ko"], v_out=out["vo"],
+                             kept_idx=out["ki"], ws=ws, score_mode=score_mode)
+
+
+def _time_compress(torch, w, kin, vin, F, T, r, out, ws, score_mode, calls, warm, reps):
+    """Mean ms of `calls` back-to-back batched compression calls, event-timed
+    on the current stream (median of `reps` repetitions after `warm`)."""
+    for _ in range(warm):
+        for _ in range(calls):
+            _compress_call(w, kin, vin, F, T, r, out, ws, score_mode)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            _compress_call(w, kin, vin, F, T, r, out, ws, score_mode)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return statistics.median(ts)
+
+
+def compress_batches(a, torch, w, S, dev):
+    """Batched World Compression beside the step: one call over 300 resident
+    units of the 1.3B-class chunk shape (3x880 tokens x 12 heads x d128, 70%
+    redundancy; 4.9 GB of keys and values, far past the last-level cache),
+    bf16 and int4 stores at r = 0.25 and 0.5, position score; GB/s of
+    algorithmic bytes from HIP events on the launch stream."""
+    c = SWEEP
+    H, D, T, F, B = c["H"], c["D"], c["T"], c["F"], c["batch"]
+    cells = {}
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        kin = torch.empty((B, F * T, H, D), dtype=torch.bfloat16, device=dev)
+        vin = torch.empty_like(kin)
+        for u in range(B):
+            kin[u], vin[u] = S.chunk_kv(3, u, 1, F, T, H, D, p_red=0.7, device=dev)
+        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T, H, D, "position"), 16),
+                         dtype=torch.uint8, device=dev)
+        for store in ("bf16", "int4"):
+            for r in (0.25, 0.5):
+                n_keep = w.wkv_keep_count(F, T, r)
+                Lc = T + n_keep
+                out = _compress_outputs(torch, B, Lc, H, D, store, dev)
+                ms = _time_compress(torch, w, kin, vin, F, T, r, out, ws, "position", 1, 2, 7)
+                nbytes = compress_bytes(c, Lc, n_keep, store == "int4") * B
+                gbps = nbytes / (ms * 1e-3) / 1e9
+                cells[f"{store} r={r}"] = {"ms": round(ms, 4), "GB": round(nbytes / 1e9, 3),
+                                           "GBps": round(gbps, 1),
+                                           "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+                del out
+        del kin, vin, ws
+    torch.cuda.synchronize()
+    return {"workload": f"{B} units of 3x880 tokens x 12 heads x d128 per call, 70% "
+                        "redundancy, position score", "cells": cells}
+
+
 def sweep(a, torch, w, S, dev):
     """wkv_compress_chunk over all 1800 units for every (redundancy, r) cell.
     300 distinct units are resident per redundancy fraction; one step
     compresses all 1800 units as 6 batched calls over them (each call streams
-    4.9 GB of keys and values, far past the last-level cache)."""
+    4.9 GB of keys and values, far past the last-level cache). After the
+    timing, the oracle compresses a few sampled units of every cell (the
+    first, the last and evenly spread ones) on the host: its time is the CPU
+    baseline and its outputs give each cell's exactness (kept sets outside the
+    1e-6 band around the selection threshold, band sizes, and bitwise outputs)."""
+    import numpy as np
     c = SWEEP
     H, D, T, F = c["H"], c["D"], c["T"], c["F"]
     B, nb = c["batch"], c["units"] // c["batch"]
+    ns = max(0, min(a.sample_units, B))
+    sample = sorted({0, B - 1} | {int(round(i * (B - 1) / max(ns - 1, 1))) for i in range(ns)}) \
+        if ns > 0 and not a.no_cpu_baseline else []
     stream = torch.cuda.Stream()
-    cells = []
+    cells, samples = [], []
+
+    def bits(t):
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)
+        return t.cpu().numpy().view(np.uint16) if t.dtype == torch.int16 else t.cpu().numpy()
+
     with torch.cuda.stream(stream):
         kin = torch.empty((B, F * T, H, D), dtype=torch.bfloat16, device=dev)
         vin = torch.empty_like(kin)
@@ -583,46 +686,23 @@ def sweep(a, torch, w, S, dev):
         for pi, p_red in enumerate(c["p_red"]):
             for u in range(B):
                 kin[u], vin[u] = S.chunk_kv(3, u, pi, F, T, H, D, p_red=p_red, device=dev)
+            src = {u: (bits(kin[u]), bits(vin[u])) for u in sample}
             for r in c["ratios"]:
                 n_keep = w.wkv_keep_count(F, T, r)
                 Lc = T + n_keep
-                ki = torch.empty((B, Lc), dtype=torch.int32, device=dev)
-                if a.store == "int4":
-                    ko = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
-                    vo = torch.empty_like(ko)
-                    ks = torch.empty((B, Lc, H, D // 32), dtype=torch.bfloat16, device=dev)
-                    vs = torch.empty_like(ks)
-                else:
-                    ko = torch.empty((B, Lc, H, D), dtype=torch.bfloat16, device=dev)
-                    vo = torch.empty_like(ko)
+                out = _compress_outputs(torch, B, Lc, H, D, a.store, dev)
+                ms = _time_compress(torch, w, kin, vin, F, T, r, out, ws, a.score_mode, nb,
+                                    max(1, a.warmup // 5), max(1, a.steps // 10))
                 unit_bytes = compress_bytes(c, Lc, n_keep, a.store == "int4")
-
-                def step():
-                    for _ in range(nb):
-                        if a.store == "int4":
-                            w.wkv_compress_chunk_int4(kin, vin, F, T, r, k_packed=ko, v_packed=vo,
-                                                      k_scale=ks, v_scale=vs, kept_idx=ki, ws=ws,
-                                                      score_mode=a.score_mode)
-                        else:
-                            w.wkv_compress_chunk(kin, vin, F, T, r, k_out=ko, v_out=vo,
-                                                 kept_idx=ki, ws=ws, score_mode=a.score_mode)
-                for _ in range(max(1, a.warmup // 5)):
-                    step()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = max(1, a.steps // 10)
-                e0.record()
-                for _ in range(reps):
-                    step()
-                e1.record()
-                torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / reps
                 gbps = unit_bytes * c["units"] / (ms * 1e-3) / 1e9
-                cells.append({"p_red": p_red, "r": r, "ms": round(ms, 3), "GB": round(unit_bytes * c["units"] / 1e9, 2),
+                cells.append({"p_red": p_red, "r": r, "ms": round(ms, 3),
+                              "GB": round(unit_bytes * c["units"] / 1e9, 2),
                               "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)})
-                del ko, vo, ki
-                if a.store == "int4":
-                    del ks, vs
+                for u in sample:
+                    samples.append(dict(cell=len(cells) - 1, unit=u, r=r, src=src[u],
+                                        out={n: bits(t[u]) for n, t in out.items()}))
+                del out
+        del kin, vin, ws
     main_cell = next(x for x in cells if x["p_red"] == 0.7 and x["r"] == 0.5)
     rec = {
         "metric": METRIC,
@@ -641,7 +721,72 @@ def sweep(a, torch, w, S, dev):
                      "frac": main_cell["frac"], "traffic": None},
         "cpu_baseline": None,
     }
+    if samples:
+        rec["cpu_baseline"] = sweep_cpu_baseline(a, c, cells, samples)
     print(json.dumps(rec), flush=True)
+
+
+def sweep_cpu_baseline(a, c, cells, samples):
+    """The oracle, as it stands, on the sampled units of every sweep cell:
+    its per-unit time (scaled to the 1800-unit step) and each cell's
+    exactness against the GPU outputs of those units."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import wkv_oracle as O
+
+    F, T = c["F"], c["T"]
+    t_all = 0.0
+    for smp in samples:
+        kb, vb = smp["src"]
+        r = smp["r"]
+        t0 = time.perf_counter()
+        if a.store == "int4":
+            ok, ov, oks, ovs, oi, osc = O.compress_chunk_int4(kb, vb, F, T, r,
+                                                              score_mode=a.score_mode)
+            ref = {"kp": ok, "vp": ov, "ks": oks, "vs": ovs}
+        else:
+            ok, ov, oi, osc = O.compress_chunk(kb, vb, F, T, r, score_mode=a.score_mode)
+            ref = {"ko": ok, "vo": ov}
+        t_all += time.perf_counter() - t0
+        g = smp["out"]
+        n_keep = O.keep_count(F, T, r)
+        N = (F - 1) * T
+        band = set()
+        if 0 < n_keep < N:
+            key = np.where(np.isnan(osc), np.inf, osc)
+            srt = np.sort(key)
+            thr = 0.5 * (srt[n_keep - 1] + srt[n_keep])
+            band = set(np.nonzero(np.abs(key - thr) <= 1e-6)[0].tolist())
+        okept = set((oi[T:] - T).tolist())
+        gkept = set((g["ki"][T:] - T).tolist())
+        outside_ok = (okept - band) == (gkept - band)
+        ndiff = len((okept ^ gkept) & band)
+        bitwise = ndiff == 0 and np.array_equal(g["ki"], oi) and all(
+            np.array_equal(g[n], ref[n]) for n in ref)
+        cell = cells[smp["cell"]]
+        st = cell.setdefault("exactness", {"units_checked": 0, "band_tokens": 0,
+                                           "band_differing": 0, "kept_exact_outside_band": True,
+                                           "outputs_bitwise": True})
+        st["units_checked"] += 1
+        st["band_tokens"] += len(band)
+        st["band_differing"] += ndiff
+        st["kept_exact_outside_band"] &= bool(outside_ok)
+        st["outputs_bitwise"] &= bool(bitwise)
+    per_unit = t_all / len(samples)
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p["num_threads"] for p in blas] or [1])
+    return {
+        "value": round(1.0 / (per_unit * c["units"]), 6),
+        "unit": "sweep cells/s (1800 units per cell)",
+        "cores": threads,
+        "cpu_model": cpu_model(),
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle compression of {len(samples)} sampled units "
+                   f"({len(samples) // max(len(cells), 1)} per cell, first and last included), "
+                   f"{per_unit:.3f} s per unit, scaled to the 1800 units of one cell"),
+        "seconds": round(t_all, 3),
+    }
 
 
 def tier_bench(a, torch, w, S, dev):
