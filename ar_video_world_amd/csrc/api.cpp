@@ -178,6 +178,44 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, i
                          kept_idx, scores, ws, ws_bytes, stream);
 }
 
+wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int32_t B,
+                                      int32_t F, int32_t T, int32_t H, int32_t D, float r,
+                                      int32_t score_mode, uint16_t* k_out, uint16_t* v_out,
+                                      int32_t* kept_idx, double* scores, wkv_stream_t stream) {
+  static const char* fn = "wkv_compress_chunk_noalloc";
+  if (!k_out || !v_out)
+    return fail(WKV_ERR_NULL, "%s: k, v, k_out, v_out and kept_idx are required", fn);
+  if (!aligned16(k_out) || !aligned16(v_out))
+    return fail(WKV_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+  // Arguments the shared checks refuse go straight to them (with no
+  // workspace), so they are reported exactly as by wkv_compress_chunk.
+  if (!k || !v || !kept_idx || (D != 64 && D != 128) || H < 1 || (int64_t)H * D > 8192 ||
+      B < 1 || B > kMaxGridYZ || F < 2 || F > 4 || T < 1 || (int64_t)(F - 1) * T > 8192 ||
+      !(r >= 0.0f && r <= 1.0f) ||
+      (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN))
+    return compress_common(fn, k, v, B, F, T, H, D, r, score_mode,
+                           wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
+                           kept_idx, scores, nullptr, 0, stream);
+  const int n_keep = (int)keep_count(F, T, r);
+  const int N = (F - 1) * T;
+  const bool score = scores != nullptr || (n_keep > 0 && n_keep < N);
+  const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
+  const size_t need = compress_ws_layout(B, F, T, H, D, mean, score && !scores).total;
+  const size_t cap = wkv::compress_scratch_bytes();
+  if (need > cap)
+    return fail(WKV_ERR_WORKSPACE,
+                "%s: this call needs %zu bytes of workspace, more than the library's static "
+                "scratch of %zu bytes (use wkv_compress_chunk with a workspace)", fn, need, cap);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = wkv::compress_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "wkv_compress_chunk_noalloc: scratch address");
+  }
+  return compress_common(fn, k, v, B, F, T, H, D, r, score_mode,
+                         wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
+                         kept_idx, scores, ws, need > 0 ? cap : 0, stream);
+}
+
 wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
                                    int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
                                    uint8_t* k_packed, uint8_t* v_packed, uint16_t* k_scale,

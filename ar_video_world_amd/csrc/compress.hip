@@ -28,6 +28,8 @@
 //            all kept V rows with 16-byte loads and stores, all streaming
 //            (plain loads of the K rows, which the score pass read before,
 //            were 2 % slower).
+#include <mutex>
+
 #include "wkv_common.hpp"
 #include "wkv_internal.hpp"
 #include "wkv_select.hpp"
@@ -611,6 +613,37 @@ int compress_score_tile(int B, int T, int H, bool grow) {
          (long long)((T + tt * 2 - 1) / (tt * 2)) * B >= 2048)
     tt *= 2;
   return tt < T ? tt : T;
+}
+
+// Workspace of wkv_compress_chunk_noalloc, for callers that cannot allocate
+// (code under graph capture, serving loops, harnesses that forbid it): every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code the array's name is not a device address; its address on the current
+// device comes from hipGetSymbolAddress, resolved once per device.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+size_t compress_scratch_bytes() { return kScratchBytes; }
+
+hipError_t compress_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int compress_mean_slices(int B, int T, int H) {

@@ -34,6 +34,13 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, i
                            int32_t* kept_idx, double* scores, bool need_scores,
                            double* mean_part, double* abar, hipStream_t s);
 
+// The compression workspace of callers that cannot allocate: a file-scope
+// device array of compress_scratch_bytes() bytes per GPU. compress_scratch()
+// gives its address on the current device (resolved on the first call per
+// device and kept).
+size_t compress_scratch_bytes();
+hipError_t compress_scratch(void** ptr);
+
 // ---- query retrieval
 int mean_rows_slices(int L);
 // part: [B][slices][H*D] float64 workspace; rows may be null (all rows).

@@ -82,6 +82,8 @@ _compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 6)
 _score_tile = _sig("wkv_compress_score_tile", _I32, [_I32] * 5)
 _compress = _sig("wkv_compress_chunk", C.c_int,
                  [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _SZ, _P])
+_compress_na = _sig("wkv_compress_chunk_noalloc", C.c_int,
+                    [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P])
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
                    _SZ, _P])
@@ -123,7 +125,7 @@ _attn_win = _sig("wkv_chunk_attention_window", C.c_int,
 
 EXPORTS = ["wkv_abi_version", "wkv_last_error", "wkv_keep_count",
            "wkv_compress_workspace_bytes", "wkv_compress_score_tile", "wkv_compress_chunk",
-           "wkv_compress_chunk_int4",
+           "wkv_compress_chunk_noalloc", "wkv_compress_chunk_int4",
            "wkv_mean_rows_workspace_bytes", "wkv_mean_rows", "wkv_query_topk", "wkv_pose_topk",
            "wkv_pose_topk_so3", "wkv_pose_topk_host", "wkv_pose_extrapolate", "wkv_tier_init", "wkv_tier_plan", "wkv_tier_prefetch",
            "wkv_tier_resolve", "wkv_window_rows",
@@ -297,6 +299,35 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     if squeeze:
         k_out, v_out, kept_idx = k_out[0], v_out[0], kept_idx[0]
         scores = None if scores is None else scores[0]
+    return k_out, v_out, kept_idx, scores
+
+
+def wkv_compress_chunk_noalloc(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
+                               k_out: torch.Tensor, v_out: torch.Tensor,
+                               kept_idx: torch.Tensor, scores=None, stream=None,
+                               score_mode="position"):
+    """wkv_compress_chunk with the library's static device workspace: no
+    device memory is allocated, so every output is passed in. k, v: bf16
+    [B, F*T, H, D]; k_out, v_out: bf16 [B, Lc, H, D]; kept_idx: int32 [B, Lc];
+    scores: optional float64 [B, (F-1)*T]. Calls that overlap on one GPU
+    share the workspace and must be ordered by the caller."""
+    _bits(k, "k"), _bits(v, "v")
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k, v: expected equal [B, F*T, H, D] shapes, got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    B, FT, H, D = k.shape
+    if FT != F * T:
+        raise ValueError(f"k has {FT} rows per unit, expected F*T={F * T}")
+    Lc = T + max(wkv_keep_count(F, T, r), 0)
+    _typed(k_out, "k_out", _BF16, (B, Lc, H, D))
+    _typed(v_out, "v_out", _BF16, (B, Lc, H, D))
+    _typed(kept_idx, "kept_idx", _I32, (B, Lc))
+    _typed(scores, "scores", (torch.float64,), (B, (F - 1) * T))
+    _on_device(("k", k), ("v", v), ("k_out", k_out), ("v_out", v_out), ("kept_idx", kept_idx),
+               ("scores", scores))
+    st = _compress_na(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode), _ptr(k_out),
+                      _ptr(v_out), _ptr(kept_idx), _ptr(scores), _stream(stream))
+    _check("wkv_compress_chunk_noalloc", st)
     return k_out, v_out, kept_idx, scores
 
 

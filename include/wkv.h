@@ -169,6 +169,23 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
                               int32_t* kept_idx, double* scores, void* ws,
                               size_t ws_bytes, wkv_stream_t stream);
 
+/* wkv_compress_chunk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a static device array
+ * of 64 MiB that every GPU the library runs on holds until the process ends;
+ * its address on a device is resolved on the first call on that device
+ * (make that first call outside graph capture). The call allocates nothing.
+ * A call whose workspace (wkv_compress_workspace_bytes, less the scores when
+ * given) exceeds 64 MiB is refused with WKV_ERR_WORKSPACE. Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (on different streams, or concurrently enqueued by
+ * other threads) race and must be ordered by the caller. Arguments, outputs,
+ * limits and other errors as wkv_compress_chunk. */
+wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int32_t B,
+                                      int32_t F, int32_t T, int32_t H, int32_t D, float r,
+                                      int32_t score_mode, uint16_t* k_out, uint16_t* v_out,
+                                      int32_t* kept_idx, double* scores, wkv_stream_t stream);
+
 /* Compress B contiguous units and store the compressed rows in the int4
  * format of the bank (wkv_bank with WKV_BANK_INT4_G32): the int4 KV store of
  * [WorldPager] (abstract, Fig. 2) written at eviction time. Selection and
