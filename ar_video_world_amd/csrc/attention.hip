@@ -26,7 +26,8 @@
 //     c = scale*log2(e), converted to bf16, and the row sum is a bf16 dot2 of
 //     exactly the weights the P*V product uses. There is no per-tile row max:
 //     the first tile of a block's key range sets mref to that tile's row max
-//     (so the row sum is >= 1 from then on and cannot underflow), and after
+//     before the key loop (so the row sum is >= 1 from then on and cannot
+//     underflow), and after
 //     that a range guard on the tile's row sums (rare branch) moves mref up
 //     only when some weight would approach the fp32/bf16 range. O and l
 //     always share mref, so the result does not depend on where it sits.
@@ -360,6 +361,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __syncthreads();
   qk(kst0, sc);
   __syncthreads();  // kst0 is refilled by the first iteration
+  // The reference starts at the first tile's row max (over its real keys),
+  // so the row's largest weight so far is 1 and its sum stays >= 1: nothing
+  // that dominates the row can underflow.
+  if (nblk > 0) {
+    int lim = kend - kbeg;
+    if constexpr (SEG) lim = min(lim, tab[kbeg / kBN].nvalid);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kt * 32 + 16 * (e >> 3) + 8 * g + (e & 7) < lim) mx = fmaxf(mx, sc[kt][e]);
+    mx = max_halves(mx) * c;
+    if (mx > -INFINITY) mref = mx;
+  }
 
   // Iteration t: loads K(t+2) and V(t+1); softmax of S(t) (registers)
   // overlapped with S^T(t+1) from K stage kc; O^T += V(t) P(t) from V stage vc.
@@ -449,21 +465,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    // First tile of the range: the reference becomes the tile's row max, so
-    // the row's largest weight so far is 1 and its sum stays >= 1 (nothing
-    // that dominates the row can underflow). Uniform branch, once per block.
-    if (it == 0) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kt][e]);
-      mx = max_halves(mx) * c;
-      if (mx > -INFINITY) {
-        mref = mx;
-        weights();
-      }
     }
     // Range guard. The reference mref stays where it is while every half-row
     // tile sum is <= 2^30 (no weight near the fp32/bf16 range). Otherwise the
