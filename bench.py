@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batches", action="store_true",
                     help="skip the batched 300-unit compression cells of the breakdown")
+    ap.add_argument("--sweep-cells", default=None,
+                    help="restrict the sweep to cells 'p_red:r,...' (e.g. 0.7:0.25,0.7:0.5)")
     ap.add_argument("--sample-units", type=int, default=30,
                     help="units per sweep cell checked against the oracle (CPU baseline leg)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -484,18 +486,7 @@ def main():
         torch.cuda.synchronize()
         t_so3 = statistics.fmean(e[0].elapsed_time(e[1]) for e in pev)
 
-        copy_gbps = None
-        if a.copy_probe:
-            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-            dst = torch.empty_like(src)
-            src.fill_(1)
-            ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ce0.record()
-            dst.copy_(src)
-            ce1.record()
-            torch.cuda.synchronize()
-            copy_gbps = 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
-            del src, dst
+        copy_gbps = _copy_probe(torch, dev) if a.copy_probe else None
 
     # batched compression of 300 units beside the step (timed cells)
     batches = None if a.no_batches else compress_batches(a, torch, w, S, dev)
@@ -577,6 +568,22 @@ def main():
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(a, c, sets[0], bank, poses, qhist, Nq, Nk, Lc)
     print(json.dumps(rec), flush=True)
+
+
+def _copy_probe(torch, dev):
+    """One plain 1 GiB device-to-device copy (the HBM counters' calibration:
+    it reads and writes exactly 2^30 bytes). Returns its GB/s."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    dst.copy_(src)
+    ce1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
 
 
 def _compress_outputs(torch, B, Lc, H, D, store, dev):
@@ -667,6 +674,9 @@ def sweep(a, torch, w, S, dev):
     c = SWEEP
     H, D, T, F = c["H"], c["D"], c["T"], c["F"]
     B, nb = c["batch"], c["units"] // c["batch"]
+    only = None
+    if a.sweep_cells:
+        only = {(float(x.split(":")[0]), float(x.split(":")[1])) for x in a.sweep_cells.split(",")}
     ns = max(0, min(a.sample_units, B))
     sample = sorted({0, B - 1} | {int(round(i * (B - 1) / max(ns - 1, 1))) for i in range(ns)}) \
         if ns > 0 and not a.no_cpu_baseline else []
@@ -684,10 +694,14 @@ def sweep(a, torch, w, S, dev):
         ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T, H, D, a.score_mode), 16),
                          dtype=torch.uint8, device=dev)
         for pi, p_red in enumerate(c["p_red"]):
+            if only is not None and not any(p == p_red for p, _ in only):
+                continue
             for u in range(B):
                 kin[u], vin[u] = S.chunk_kv(3, u, pi, F, T, H, D, p_red=p_red, device=dev)
             src = {u: (bits(kin[u]), bits(vin[u])) for u in sample}
             for r in c["ratios"]:
+                if only is not None and (p_red, r) not in only:
+                    continue
                 n_keep = w.wkv_keep_count(F, T, r)
                 Lc = T + n_keep
                 out = _compress_outputs(torch, B, Lc, H, D, a.store, dev)
@@ -703,7 +717,9 @@ def sweep(a, torch, w, S, dev):
                                         out={n: bits(t[u]) for n, t in out.items()}))
                 del out
         del kin, vin, ws
-    main_cell = next(x for x in cells if x["p_red"] == 0.7 and x["r"] == 0.5)
+        if a.copy_probe:
+            _copy_probe(torch, dev)
+    main_cell = next((x for x in cells if x["p_red"] == 0.7 and x["r"] == 0.5), cells[0])
     rec = {
         "metric": METRIC,
         "value": main_cell["GBps"],
