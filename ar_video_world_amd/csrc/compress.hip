@@ -11,7 +11,8 @@
 //            exact in float64), reduces across its 4 lanes, and stores the
 //            per-head cosine in LDS; the block then averages over heads in a
 //            fixed order. The anchor slice already sits in registers, so the
-//            score kernel also writes the anchor rows of k_out.
+//            score kernel also writes the anchor rows of k_out, through a
+//            per-wave LDS stage so that every store writes whole lines.
 //            With the anchor-mean score (the section's equation: the mean
 //            cosine to all T anchor tokens) two kernels run first instead:
 //            anchor-mean sums, per run of anchor tokens of one unit (all
@@ -149,28 +150,71 @@ struct CompressOut {
   uint16_t* vs;
 };
 
-// Stores the (row, head) slice a quad holds (lane `sub` has 16-byte pieces
-// i at elements sub*8 + i*32) at element offset `e0` = (row*H + h)*D of a
-// unit's output, as bf16 or int4.
+// Wave-staged stores of the (row, head) slices held by the 16 quads of a
+// wave. The quads hold 16 consecutive (row, head) pairs, so their output is
+// one contiguous run: each active quad writes its slice (bf16 rows, or int4
+// codes and scales) into the wave's LDS stage, then every lane stores whole
+// 16-byte pieces of the run (the int4 scales as one 8- or 4-byte piece per
+// pair), so each store instruction writes whole cache lines. Storing the
+// slices from the quads directly wrote 16-byte pieces at 64- or 256-byte
+// strides, partial lines that cost a 300-unit call of 3 x 880 x 12 x 128
+// 110-170 us.
 template <int NLD, bool Q4>
-__device__ __forceinline__ void store_slice(const uint4 (&a)[NLD], size_t e0, int sub,
+struct SliceStage {
+  static constexpr int SLICE = Q4 ? NLD * 16 : NLD * 64;  // bytes per slice: codes, or bf16
+  static constexpr int SCALE = NLD * 2;                   // int4 scale bytes per slice
+  static constexpr int BYTES = 16 * (SLICE + (Q4 ? SCALE : 0));  // one wave's stage
+};
+
+// Every lane of the wave calls this (the stores are wave-wide). `active`:
+// this quad holds a slice (quad-uniform); qw: the quad's index in the wave;
+// nvalid: how many of the wave's 16 pairs are stored; e0: element offset of
+// the wave's first pair in the output ((row*H + h)*D).
+template <int NLD, bool Q4>
+__device__ __forceinline__ void stage_store(const uint4 (&a)[NLD], bool active, int qw, int sub,
+                                            int lane, uint8_t* stage, int nvalid, size_t e0,
                                             uint16_t* bf, uint8_t* pk, uint16_t* sc) {
-  if constexpr (!Q4) {
+  using SS = SliceStage<NLD, Q4>;
+  if (active) {
+    if constexpr (!Q4) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) st_stream(bf + e0 + sub * 8 + i * 32, a[i]);
-  } else {
+      for (int i = 0; i < NLD; ++i)
+        *reinterpret_cast<uint4*>(stage + qw * SS::SLICE + i * 64 + sub * 16) = a[i];
+    } else {
+      uint8_t* scl = stage + 16 * SS::SLICE;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      uint16_t sb;
-      const uint32_t p = int4_encode_quad(a[i], &sb);
-      // Plain stores: a (row, head) slice is a piece of a cache line whose
-      // other pieces come from other quads and blocks, and L2 merges them
-      // (streaming these pieces ran the anchor-mean int4 batch at 0.36 of HBM
-      // peak against 0.49).
-      *reinterpret_cast<uint32_t*>(pk + e0 / 2 + i * 16 + sub * 4) = p;
-      if (sub == 0) sc[e0 / 32 + i] = sb;
+      for (int i = 0; i < NLD; ++i) {
+        uint16_t sb;
+        const uint32_t p = int4_encode_quad(a[i], &sb);
+        *reinterpret_cast<uint32_t*>(stage + qw * SS::SLICE + i * 16 + sub * 4) = p;
+        if (sub == 0) *reinterpret_cast<uint16_t*>(scl + qw * SS::SCALE + i * 2) = sb;
+      }
     }
   }
+  // The wave's LDS writes land before its reads (LDS requests of one wave
+  // complete in issue order; the wait also orders them for the compiler).
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  if constexpr (!Q4) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(bf) + e0 * 2;
+    for (int o = lane * 16; o < nvalid * SS::SLICE; o += kWave * 16)
+      st_stream(dst + o, *reinterpret_cast<const uint4*>(stage + o));
+  } else {
+    uint8_t* dst = pk + e0 / 2;
+    for (int o = lane * 16; o < nvalid * SS::SLICE; o += kWave * 16)
+      st_stream(dst + o, *reinterpret_cast<const uint4*>(stage + o));
+    const uint8_t* scl = stage + 16 * SS::SLICE;
+    uint8_t* sdst = reinterpret_cast<uint8_t*>(sc) + e0 / 16;  // 2 bytes per 32 elements
+    if (lane < nvalid) {
+      if constexpr (SS::SCALE == 8)
+        *reinterpret_cast<uint2*>(sdst + lane * 8) = *reinterpret_cast<const uint2*>(scl + lane * 8);
+      else
+        *reinterpret_cast<uint32_t*>(sdst + lane * 4) = *reinterpret_cast<const uint32_t*>(scl + lane * 4);
+    }
+  }
+  // Every lane has read the stage before any quad writes it again.
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Anchor-mean blocks: 256 lanes, or 512 when 256 would leave over an eighth
@@ -210,7 +254,7 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
   constexpr int NLD = D / 32;
   constexpr int E = NLD * 8;  // elements per lane
   constexpr int NQ = NT / kLanesPerPair;
-  extern __shared__ double red[];  // [H][D]
+  extern __shared__ double red[];  // [H][D], then the waves' slice stages
   const int sl = blockIdx.x, b = blockIdx.y;
   const int P = NQ / H;  // tokens per pass (H <= NQ)
   const int j0 = sl * mt;
@@ -233,14 +277,28 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
 #pragma unroll
     for (int i = 0; i < NLD; ++i) an[i] = *reinterpret_cast<const uint4*>(unit + off + i * 32);
   };
-  const int first = t < P ? t : ntok;  // quads past the last full head set idle
-  if (first < ntok) load_row(first);
-  for (int jl = first; jl < ntok; jl += P) {
+  // Quads past the last full head set idle. Passes run together over the
+  // block (pass k takes tokens kP .. kP+P-1, all heads: P*H consecutive
+  // (row, head) slices), so each wave's anchor slices leave through its stage.
+  uint8_t* stage = reinterpret_cast<uint8_t*>(red + (size_t)H * D) +
+                   (tid / kWave) * SliceStage<NLD, Q4>::BYTES;
+  const int qw = q % 16;
+  const int wq0 = q - qw;  // the wave's first quad
+  if (t < P && t < ntok) load_row(t);
+  for (int k0 = 0; k0 < ntok; k0 += P) {
+    const int jl = k0 + t;
+    const bool act = t < P && jl < ntok;
     uint4 a[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) a[i] = an[i];
-    if (jl + P < ntok) load_row(jl + P);
-    store_slice<NLD, Q4>(a, ubase + ((size_t)(j0 + jl) * H + h) * D, sub, out.k, out.kq, out.ks);
+    if (act && jl + P < ntok) load_row(jl + P);
+    // this wave's slices: quads wq0 .. wq0+15 of the pass, while they hold a
+    // token of the block
+    const int nv = min(16, min(P * H, (ntok - k0) * H) - wq0);
+    if (nv > 0)
+      stage_store<NLD, Q4>(a, act, qw, sub, tid % kWave, stage, nv,
+                           ubase + ((size_t)(j0 + k0) * H + wq0) * D, out.k, out.kq, out.ks);
+    if (!act) continue;
     double na = 0.0;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
@@ -296,8 +354,13 @@ __global__ void compress_anchor_mean_final_kernel(const double* __restrict__ par
 }
 
 // grid: (ceil(T / TT), B). Dynamic LDS: TT * (F-1) * H doubles, then (MEAN)
-// H rows of D + kAbarSkew doubles holding abar.
+// H rows of D + kAbarSkew doubles holding abar, or (position score) from the
+// next 16-byte boundary the 4 waves' slice stages.
 constexpr int kAbarSkew = 2;
+
+__host__ __device__ inline size_t score_stage_offset(int TT, int F, int H) {
+  return ((size_t)TT * (F - 1) * H * sizeof(double) + 15) / 16 * 16;
+}
 
 template <int D, int F, bool MEAN, bool Q4>
 __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
@@ -396,9 +459,16 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
       }
     };
     if (slot < npairs) load_rows(slot);
-    // Every lane of a quad runs the same number of iterations, so the quad
-    // shuffles below always see their partners.
-    for (int pair = slot; pair < npairs; pair += kPairsPerPass) {
+    // Each wave walks its passes together (the anchor slices leave through
+    // the wave's stage); a quad with no pair in a pass only joins the store.
+    // The 4 lanes of a quad always agree, so the quad shuffles below always
+    // see their partners.
+    uint8_t* stage = reinterpret_cast<uint8_t*>(cosbuf) + score_stage_offset(TT, F, H) +
+                     (tid / kWave) * SliceStage<NLD, Q4>::BYTES;
+    const int qw = slot % 16;
+    for (int pw = slot - qw; pw < npairs; pw += kPairsPerPass) {
+      const int pair = pw + qw;
+      const bool act = pair < npairs;
       const int jl = pair / H;
       const int h = pair - jl * H;
       uint4 ac[NLD];
@@ -409,9 +479,10 @@ __global__ __launch_bounds__(kScoreBlock) void compress_score_kernel(
       for (int f = 0; f < F - 1; ++f)
 #pragma unroll
         for (int i = 0; i < NLD; ++i) xc[f][i] = x[f][i];
-      if (pair + kPairsPerPass < npairs) load_rows(pair + kPairsPerPass);
-      store_slice<NLD, Q4>(ac, ubase + ((size_t)(j0 + jl) * H + h) * D, sub, out.k, out.kq,
-                           out.ks);
+      if (act && pair + kPairsPerPass < npairs) load_rows(pair + kPairsPerPass);
+      stage_store<NLD, Q4>(ac, act, qw, sub, tid % kWave, stage, min(16, npairs - pw),
+                           ubase + ((size_t)j0 * H + pw) * D, out.k, out.kq, out.ks);
+      if (!act) continue;
       double na = 0.0;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) accum_sq(ac[i], na);
@@ -546,15 +617,20 @@ hipError_t launch_score(const uint16_t* k, int B, int T, int H, int TT, double* 
                         const CompressOut& out, bool q4, int Lc, const double* abar,
                         hipStream_t s) {
   dim3 grid((T + TT - 1) / TT, B);
-  size_t lds = (size_t)TT * (F - 1) * H * sizeof(double);
+  const size_t cos_lds = (size_t)TT * (F - 1) * H * sizeof(double);
+  const size_t stage_lds = score_stage_offset(TT, F, H);
+  constexpr int NLD = D / 32;
+  constexpr int W = kScoreBlock / kWave;
   if (abar) {  // the anchor-mean kernel has stored the anchor rows
-    lds += (size_t)H * (D + kAbarSkew) * sizeof(double);
+    const size_t lds = cos_lds + (size_t)H * (D + kAbarSkew) * sizeof(double);
     hipLaunchKernelGGL((compress_score_kernel<D, F, true, false>), grid, dim3(kScoreBlock), lds,
                        s, k, T, H, TT, scores, out, Lc, abar);
   } else if (q4) {
+    const size_t lds = stage_lds + W * SliceStage<NLD, true>::BYTES;
     hipLaunchKernelGGL((compress_score_kernel<D, F, false, true>), grid, dim3(kScoreBlock), lds,
                        s, k, T, H, TT, scores, out, Lc, abar);
   } else {
+    const size_t lds = stage_lds + W * SliceStage<NLD, false>::BYTES;
     hipLaunchKernelGGL((compress_score_kernel<D, F, false, false>), grid, dim3(kScoreBlock),
                        lds, s, k, T, H, TT, scores, out, Lc, abar);
   }
@@ -578,7 +654,9 @@ void launch_anchor_mean_nt(const uint16_t* k, int B, int F, int T, int H, double
                            const CompressOut& out, bool q4, int Lc, hipStream_t s) {
   const int mt = compress_mean_tokens(B, T, H);
   const dim3 grid((T + mt - 1) / mt, B);
-  const size_t lds = (size_t)H * D * sizeof(double);
+  constexpr int W = NT / kWave;
+  const size_t lds = (size_t)H * D * sizeof(double) +
+                     W * (q4 ? SliceStage<D / 32, true>::BYTES : SliceStage<D / 32, false>::BYTES);
   if (q4)
     hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true, NT>), grid, dim3(NT), lds, s, k, F,
                        T, H, mt, part, out, Lc);
@@ -653,7 +731,11 @@ int compress_mean_slices(int B, int T, int H) {
 
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4) {
   const int TT = compress_score_tile(B, T, H, q4 || mean);
-  return ((size_t)TT * (F - 1) * H + (mean ? (size_t)H * (D + kAbarSkew) : 0)) * sizeof(double);
+  if (mean) return ((size_t)TT * (F - 1) * H + (size_t)H * (D + kAbarSkew)) * sizeof(double);
+  const int W = kScoreBlock / kWave;
+  const size_t stage = D == 128 ? (q4 ? SliceStage<4, true>::BYTES : SliceStage<4, false>::BYTES)
+                                : (q4 ? SliceStage<2, true>::BYTES : SliceStage<2, false>::BYTES);
+  return score_stage_offset(TT, F, H) + W * stage;
 }
 
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
