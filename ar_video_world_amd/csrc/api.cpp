@@ -78,18 +78,26 @@ constexpr int kMaxGridYZ = 65535;
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-// Workspace layout: [scores B*N][anchor-mean partials B*H*slices*D][abar B*H*D],
-// float64, each part 256-byte aligned; the last two for the anchor-mean score.
+// Workspace layout, float64, each part 256-byte aligned:
+//   [scores B*N]                        when the caller gives no scores output
+//   [anchor-mean partials B*H*slices*D] [abar B*H*D]   anchor-mean score
+//   [anchor-row sums B*H*slices*D]      mean key with the anchor-mean score
+//   [kept-row run sums B*runs*H*D]      mean key
 struct CompressWsLayout {
-  size_t scores, part, abar, total;
+  size_t scores, part, abar, araw, ksum, total;
 };
 CompressWsLayout compress_ws_layout(int32_t B, int32_t F, int32_t T, int32_t H, int32_t D,
-                                    bool mean, bool scores_in_ws) {
+                                    bool mean, bool scores_in_ws, bool key_mean) {
   CompressWsLayout L{};
+  const size_t slices = (size_t)B * H * wkv::compress_mean_slices(B, T, H) * D * sizeof(double);
   L.scores = 0;
   L.part = scores_in_ws ? round_up((size_t)B * (size_t)(F - 1) * (size_t)T * sizeof(double)) : 0;
-  L.abar = L.part + (mean ? round_up((size_t)B * H * wkv::compress_mean_slices(B, T, H) * D * sizeof(double)) : 0);
-  L.total = L.abar + (mean ? round_up((size_t)B * H * D * sizeof(double)) : 0);
+  L.abar = L.part + (mean ? round_up(slices) : 0);
+  L.araw = L.abar + (mean ? round_up((size_t)B * H * D * sizeof(double)) : 0);
+  L.ksum = L.araw + (key_mean && mean ? round_up(slices) : 0);
+  L.total = L.ksum + (key_mean ? round_up((size_t)B * wkv::compress_key_runs_max(B, F, T, H * D / 8) *
+                                          (size_t)H * D * sizeof(double))
+                               : 0);
   return L;
 }
 
@@ -98,7 +106,8 @@ CompressWsLayout compress_ws_layout(int32_t B, int32_t F, int32_t T, int32_t H, 
 wkv_status compress_common(const char* fn, const uint16_t* k, const uint16_t* v, int32_t B,
                            int32_t F, int32_t T, int32_t H, int32_t D, float r,
                            int32_t score_mode, const wkv::CompressDst& dst, int32_t* kept_idx,
-                           double* scores, void* ws, size_t ws_bytes, wkv_stream_t stream) {
+                           double* scores, double* key_mean, void* ws, size_t ws_bytes,
+                           wkv_stream_t stream) {
   if (!k || !v || !kept_idx)
     return fail(WKV_ERR_NULL, "%s: k, v and kept_idx are required", fn);
   if (wkv_status st = check_hd(H, D)) return st;
@@ -113,26 +122,33 @@ wkv_status compress_common(const char* fn, const uint16_t* k, const uint16_t* v,
   if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN)
     return fail(WKV_ERR_UNSUPPORTED, "%s: score_mode=%d (supported: 0, 1)", fn, score_mode);
   if (!aligned16(k) || !aligned16(v) || !aligned16(kept_idx) || (scores && !aligned16(scores)) ||
-      (ws && !aligned16(ws)))
+      (key_mean && !aligned16(key_mean)) || (ws && !aligned16(ws)))
     return fail(WKV_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
   const int n_keep = (int)keep_count(F, T, r);
   const int N = (F - 1) * T;
   const bool need_scores = scores != nullptr;
   const bool score = need_scores || (n_keep > 0 && n_keep < N);
   const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
-  const CompressWsLayout L = compress_ws_layout(B, F, T, H, D, mean, score && !scores);
+  const CompressWsLayout L =
+      compress_ws_layout(B, F, T, H, D, mean, score && !scores, key_mean != nullptr);
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(WKV_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn,
                 ws ? ws_bytes : (size_t)0, L.total);
   if (score && wkv::compress_score_lds_bytes(B, F, T, H, D, mean, dst.k_packed != nullptr) >
                    (size_t)max_lds_per_block())
     return fail(WKV_ERR_SHAPE, "%s: H*D too large for the score kernel's LDS", fn);
+  if (mean &&
+      wkv::compress_anchor_lds_bytes(H, D, dst.k_packed != nullptr) > (size_t)max_lds_per_block())
+    return fail(WKV_ERR_SHAPE, "%s: H*D too large for the anchor kernel's LDS", fn);
   char* wsb = static_cast<char*>(ws);
   double* sbuf = scores ? scores : (score ? reinterpret_cast<double*>(wsb + L.scores) : nullptr);
   double* part = mean ? reinterpret_cast<double*>(wsb + L.part) : nullptr;
   double* abar = mean ? reinterpret_cast<double*>(wsb + L.abar) : nullptr;
+  const wkv::KeyMeanWs km{key_mean,
+                          key_mean && mean ? reinterpret_cast<double*>(wsb + L.araw) : nullptr,
+                          key_mean ? reinterpret_cast<double*>(wsb + L.ksum) : nullptr};
   hipError_t e = wkv::compress_launch(k, v, B, F, T, H, D, n_keep, dst, kept_idx, sbuf,
-                                      need_scores, part, abar, static_cast<hipStream_t>(stream));
+                                      need_scores, part, abar, km, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return WKV_OK;
 }
@@ -159,23 +175,25 @@ int32_t wkv_compress_score_tile(int32_t B, int32_t T, int32_t H, int32_t score_m
 }
 
 size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H, int32_t D,
-                                    int32_t score_mode) {
+                                    int32_t score_mode, int32_t key_mean) {
   if (B < 1 || F < 2 || T < 1 || H < 1 || D < 1) return 0;
   if (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN) return 0;
-  return compress_ws_layout(B, F, T, H, D, score_mode == WKV_SCORE_ANCHOR_MEAN, true).total;
+  return compress_ws_layout(B, F, T, H, D, score_mode == WKV_SCORE_ANCHOR_MEAN, true,
+                            key_mean != 0)
+      .total;
 }
 
 wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
                               int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
                               uint16_t* k_out, uint16_t* v_out, int32_t* kept_idx, double* scores,
-                              void* ws, size_t ws_bytes, wkv_stream_t stream) {
+                              double* key_mean, void* ws, size_t ws_bytes, wkv_stream_t stream) {
   if (!k_out || !v_out)
     return fail(WKV_ERR_NULL, "wkv_compress_chunk: k, v, k_out, v_out and kept_idx are required");
   if (!aligned16(k_out) || !aligned16(v_out))
     return fail(WKV_ERR_ALIGN, "wkv_compress_chunk: device pointers must be 16-byte aligned");
   return compress_common("wkv_compress_chunk", k, v, B, F, T, H, D, r, score_mode,
                          wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
-                         kept_idx, scores, ws, ws_bytes, stream);
+                         kept_idx, scores, key_mean, ws, ws_bytes, stream);
 }
 
 wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int32_t B,
@@ -195,12 +213,12 @@ wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int3
       (score_mode != WKV_SCORE_POSITION && score_mode != WKV_SCORE_ANCHOR_MEAN))
     return compress_common(fn, k, v, B, F, T, H, D, r, score_mode,
                            wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
-                           kept_idx, scores, nullptr, 0, stream);
+                           kept_idx, scores, nullptr, nullptr, 0, stream);
   const int n_keep = (int)keep_count(F, T, r);
   const int N = (F - 1) * T;
   const bool score = scores != nullptr || (n_keep > 0 && n_keep < N);
   const bool mean = score_mode == WKV_SCORE_ANCHOR_MEAN && score;
-  const size_t need = compress_ws_layout(B, F, T, H, D, mean, score && !scores).total;
+  const size_t need = compress_ws_layout(B, F, T, H, D, mean, score && !scores, false).total;
   const size_t cap = wkv::compress_scratch_bytes();
   if (need > cap)
     return fail(WKV_ERR_WORKSPACE,
@@ -213,14 +231,15 @@ wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int3
   }
   return compress_common(fn, k, v, B, F, T, H, D, r, score_mode,
                          wkv::CompressDst{k_out, v_out, nullptr, nullptr, nullptr, nullptr},
-                         kept_idx, scores, ws, need > 0 ? cap : 0, stream);
+                         kept_idx, scores, nullptr, ws, need > 0 ? cap : 0, stream);
 }
 
 wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t B, int32_t F,
                                    int32_t T, int32_t H, int32_t D, float r, int32_t score_mode,
                                    uint8_t* k_packed, uint8_t* v_packed, uint16_t* k_scale,
-                                   uint16_t* v_scale, int32_t* kept_idx, double* scores, void* ws,
-                                   size_t ws_bytes, wkv_stream_t stream) {
+                                   uint16_t* v_scale, int32_t* kept_idx, double* scores,
+                                   double* key_mean, void* ws, size_t ws_bytes,
+                                   wkv_stream_t stream) {
   if (!k_packed || !v_packed || !k_scale || !v_scale)
     return fail(WKV_ERR_NULL,
                 "wkv_compress_chunk_int4: k, v, k_packed, v_packed, k_scale, v_scale and kept_idx "
@@ -229,7 +248,7 @@ wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t
     return fail(WKV_ERR_ALIGN, "wkv_compress_chunk_int4: device pointers must be 16-byte aligned");
   return compress_common("wkv_compress_chunk_int4", k, v, B, F, T, H, D, r, score_mode,
                          wkv::CompressDst{nullptr, nullptr, k_packed, v_packed, k_scale, v_scale},
-                         kept_idx, scores, ws, ws_bytes, stream);
+                         kept_idx, scores, key_mean, ws, ws_bytes, stream);
 }
 
 size_t wkv_mean_rows_workspace_bytes(int32_t B, int32_t L, int32_t H, int32_t D) {

@@ -29,6 +29,7 @@
 //            all kept V rows with 16-byte loads and stores, all streaming
 //            (plain loads of the K rows, which the score pass read before,
 //            were 2 % slower).
+#include <algorithm>
 #include <mutex>
 
 #include "wkv_common.hpp"
@@ -247,12 +248,16 @@ int compress_mean_tokens(int B, int T, int H) {
 // with other heads' blocks: 465 against 325 us for the bf16 store on 300
 // units of 3 x 880 x 12 x 128). The P quads of a head add into LDS in a fixed
 // order, so the result does not depend on timing.
-template <int D, bool Q4, int NT>
+// SUMS: bit 0 = the unit anchor keys (the anchor-mean score) into part,
+// bit 1 = the anchor keys themselves (the compressed chunk's mean key) into
+// rawpart, both [B][H][slices][D].
+template <int D, bool Q4, int NT, int SUMS>
 __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
     const uint16_t* __restrict__ k, int F, int T, int H, int mt, double* __restrict__ part,
-    CompressOut out, int Lc) {
+    double* __restrict__ rawpart, CompressOut out, int Lc) {
   constexpr int NLD = D / 32;
   constexpr int E = NLD * 8;  // elements per lane
+  constexpr bool UNIT = SUMS & 1, RAW = SUMS & 2;
   constexpr int NQ = NT / kLanesPerPair;
   extern __shared__ double red[];  // [H][D], then the waves' slice stages
   const int sl = blockIdx.x, b = blockIdx.y;
@@ -266,9 +271,12 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
   const size_t HD = (size_t)H * D;
   const uint16_t* unit = k + (size_t)b * F * T * HD;
   const size_t ubase = (size_t)b * Lc * HD;  // element offset of this unit's output
-  double acc[E];
+  double acc[UNIT ? E : 1], raw[RAW ? E : 1];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0;
+  for (int e = 0; e < E; ++e) {
+    if constexpr (UNIT) acc[e] = 0.0;
+    if constexpr (RAW) raw[e] = 0.0;
+  }
   // Every lane of a quad runs the same iterations (quad shuffles inside);
   // the next token's slice is loaded while this one is reduced.
   uint4 an[NLD];
@@ -299,39 +307,58 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
       stage_store<NLD, Q4>(a, act, qw, sub, tid % kWave, stage, nv,
                            ubase + ((size_t)(j0 + k0) * H + wq0) * D, out.k, out.kq, out.ks);
     if (!act) continue;
-    double na = 0.0;
+    if constexpr (RAW) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
-    na = quad_sum(na);
-    const double inv = (na == 0.0) ? 0.0 : 1.0 / sqrt(na);
+      for (int i = 0; i < NLD; ++i) {
+        const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+        for (int c = 0; c < 4; ++c) {
+          raw[i * 8 + 2 * c] += (double)bf16_to_f32(w[c] & 0xFFFFu);
+          raw[i * 8 + 2 * c + 1] += (double)bf16_to_f32(w[c] >> 16);
+        }
+      }
+    }
+    if constexpr (UNIT) {
+      double na = 0.0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[i * 8 + 2 * c] = fma((double)bf16_to_f32(w[c] & 0xFFFFu), inv, acc[i * 8 + 2 * c]);
-        acc[i * 8 + 2 * c + 1] = fma((double)bf16_to_f32(w[c] >> 16), inv, acc[i * 8 + 2 * c + 1]);
+      for (int i = 0; i < NLD; ++i) accum_sq(a[i], na);
+      na = quad_sum(na);
+      const double inv = (na == 0.0) ? 0.0 : 1.0 / sqrt(na);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[i * 8 + 2 * c] = fma((double)bf16_to_f32(w[c] & 0xFFFFu), inv, acc[i * 8 + 2 * c]);
+          acc[i * 8 + 2 * c + 1] = fma((double)bf16_to_f32(w[c] >> 16), inv, acc[i * 8 + 2 * c + 1]);
+        }
       }
     }
   }
-  // Pass slot 0 writes each head's D sums, slots 1..P-1 add theirs in turn.
-  for (int r = 0; r < P; ++r) {
-    if (t == r) {
+  // Pass slot 0 writes each head's D sums, slots 1..P-1 add theirs in turn;
+  // then the block's sums go to its slice of the partials.
+  auto combine = [&](const double (&v)[E], double* out_part) {
+    for (int r = 0; r < P; ++r) {
+      if (t == r) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i)
+        for (int i = 0; i < NLD; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          double* cell = red + h * D + i * 32 + sub * 8 + e;
-          *cell = (r == 0) ? acc[i * 8 + e] : *cell + acc[i * 8 + e];
-        }
+          for (int e = 0; e < 8; ++e) {
+            double* cell = red + h * D + i * 32 + sub * 8 + e;
+            *cell = (r == 0) ? v[i * 8 + e] : *cell + v[i * 8 + e];
+          }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  double* dst = part + (size_t)b * HD * gridDim.x;
-  for (int i = tid; i < (int)HD; i += NT) {
-    const int hh = i / D, d = i - hh * D;
-    dst[((size_t)hh * gridDim.x + sl) * D + d] = red[i];
-  }
+    double* dst = out_part + (size_t)b * HD * gridDim.x;
+    for (int i = tid; i < (int)HD; i += NT) {
+      const int hh = i / D, d = i - hh * D;
+      dst[((size_t)hh * gridDim.x + sl) * D + d] = red[i];
+    }
+    __syncthreads();  // red is reused by the next combine
+  };
+  if constexpr (UNIT) combine(acc, part);
+  if constexpr (RAW) combine(raw, rawpart);
 }
 
 // grid: (H, B), block D. abar[b][h][d] = (sum over slices, in order) / T.
@@ -576,13 +603,14 @@ constexpr int kGatherUnroll = 3;
 // int4 store that matters most: its 4-byte code and 2-byte scale stores as
 // plain stores held a 300-unit batch at r = 1 to 0.56 of HBM peak, against
 // 0.70 streamed.
+// z0 = 1 launches the V rows only (grid z = 1).
 template <bool Q4>
 __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kept_idx, int FT, int Lc, int cpr, int k_skip,
-    CompressOut out) {
+    CompressOut out, int z0) {
   const int b = blockIdx.y;
-  const bool isk = blockIdx.z == 0;
+  const bool isk = blockIdx.z + z0 == 0;
   const int row = blockIdx.x;
   if (row >= Lc || (isk && row < k_skip)) return;  // whole block
   const uint4* src = reinterpret_cast<const uint4*>(isk ? k : v) +
@@ -610,6 +638,139 @@ __global__ __launch_bounds__(kGatherBlock) void compress_gather_kernel(
       }
     }
   }
+}
+
+// K rows of the compressed chunk with their float64 sum, for the mean key.
+// grid: (runs, column slices, B); kKsumWaves waves per block. A block takes
+// output rows [r_first + run * kKsumWaves * rw, + kKsumWaves * rw) of its
+// unit over one slice of 64 * kGatherUnroll 16-byte chunks (8 elements
+// each); wave w takes every kKsumWaves-th row from the w-th, copies it to the
+// output when its index is >= store_from (rows below were written by the
+// score kernel: bf16, or int4 encoded as in the gather kernel) and adds it
+// into float64 sums, 8 per chunk and lane. Each wave keeps its next two rows
+// in flight. The waves' sums then meet in one LDS row, added in wave order,
+// so ksum[b][run][chunk*8 ..] is a deterministic partial, added in run order
+// by the finalize kernel.
+constexpr int kKsumWaves = 4;
+constexpr int kKsumBlock = kKsumWaves * kWave;
+
+template <bool Q4>
+__global__ __launch_bounds__(kKsumBlock) void compress_gather_ksum_kernel(
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ kept_idx, int FT, int Lc,
+    int cpr, int r_first, int rw, int store_from, CompressOut out, double* __restrict__ ksum) {
+  __shared__ double red[64 * kGatherUnroll * 8];
+  const int run = blockIdx.x, cs = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  const int blk0 = r_first + run * kKsumWaves * rw;
+  const int row1 = min(Lc, blk0 + kKsumWaves * rw);
+  const int c0 = cs * 64 * kGatherUnroll + lane;
+  const uint4* src_unit = reinterpret_cast<const uint4*>(k) + (size_t)b * FT * cpr;
+  const int32_t* ki = kept_idx + (size_t)b * Lc;
+  double acc[kGatherUnroll][8];
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0;
+  auto load = [&](int row, uint4 (&dst)[kGatherUnroll]) {
+    const uint4* src = src_unit + (size_t)ki[row] * cpr;
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + 64 * u;
+      dst[u] = c < cpr ? ld_stream(src + c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  constexpr int S = kKsumWaves;  // row stride of a wave
+  const int row0 = blk0 + wv;
+  uint4 n1[kGatherUnroll], n2[kGatherUnroll];
+  if (row0 < row1) load(row0, n1);
+  if (row0 + S < row1) load(row0 + S, n2);
+  for (int row = row0; row < row1; row += S) {
+    uint4 x[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      x[u] = n1[u];
+      n1[u] = n2[u];
+    }
+    if (row + 2 * S < row1) load(row + 2 * S, n2);
+    const size_t ro = ((size_t)b * Lc + row) * cpr;
+    const bool st = row >= store_from;
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= cpr) continue;  // uniform over each quad (cpr % 4 == 0, slices of 192)
+      if (st) {
+        if constexpr (!Q4) {
+          st_stream(reinterpret_cast<uint4*>(out.k) + ro + c, x[u]);
+        } else {
+          uint16_t sb;
+          const uint32_t p = int4_encode_quad(x[u], &sb);
+          __builtin_nontemporal_store(p, reinterpret_cast<uint32_t*>(out.kq) + ro + c);
+          if ((c & 3) == 0) __builtin_nontemporal_store(sb, out.ks + (ro + c) / 4);
+        }
+      }
+      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[u][2 * q] += (double)bf16_to_f32(w[q] & 0xFFFFu);
+        acc[u][2 * q + 1] += (double)bf16_to_f32(w[q] >> 16);
+      }
+    }
+  }
+  // wave 0 writes its sums, waves 1 .. kKsumWaves-1 add theirs in turn
+  for (int j = 0; j < kKsumWaves; ++j) {
+    if (wv == j) {
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double* cell = red + (u * 64 + lane) * 8 + e;
+          *cell = (j == 0) ? acc[u][e] : *cell + acc[u][e];
+        }
+    }
+    __syncthreads();
+  }
+  double* dst = ksum + ((size_t)b * gridDim.x + run) * (size_t)cpr * 8;
+  const int nval = min(cpr - cs * 64 * kGatherUnroll, 64 * kGatherUnroll) * 8;
+  for (int i = threadIdx.x; i < nval; i += kKsumBlock)
+    dst[(size_t)cs * 64 * kGatherUnroll * 8 + i] = red[i];
+}
+
+// grid: (H, B), block D * kFinalGroups. key_mean[b][h][d] = (sum of the
+// partials) / Lc, the partials being the anchor-row slices apart[b][h][s][d]
+// (s < nslice) followed by the kept-row runs ksum[b][r][h*D + d] (r < nruns).
+// Group g adds partials g, g + G, ... in order, four loads in flight; the
+// groups' sums are then added in group order.
+constexpr int kFinalGroups = 8;
+
+__global__ __launch_bounds__(128 * kFinalGroups) void compress_key_mean_final_kernel(
+    const double* __restrict__ apart, int nslice, const double* __restrict__ ksum, int nruns,
+    int Lc, int H, double* __restrict__ key_mean) {
+  __shared__ double red[kFinalGroups][128];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int D = blockDim.x / kFinalGroups;
+  const int d = threadIdx.x % D, g = threadIdx.x / D;
+  const size_t HD = (size_t)H * D;
+  const double* ap = nslice > 0 ? apart + ((size_t)b * H + h) * nslice * D + d : nullptr;
+  const double* kp = nruns > 0 ? ksum + (size_t)b * nruns * HD + (size_t)h * D + d : nullptr;
+  auto part = [&](int p) { return p < nslice ? ap[(size_t)p * D] : kp[(size_t)(p - nslice) * HD]; };
+  const int n = nslice + nruns;
+  double t = 0.0;
+  int p = g;
+  for (; p + 3 * kFinalGroups < n; p += 4 * kFinalGroups) {
+    double x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = part(p + i * kFinalGroups);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t += x[i];
+  }
+  for (; p < n; p += kFinalGroups) t += part(p);
+  red[g][d] = t;
+  __syncthreads();
+  if (g > 0) return;
+  double s = red[0][d];
+#pragma unroll
+  for (int j = 1; j < kFinalGroups; ++j) s += red[j][d];
+  key_mean[((size_t)b * H + h) * D + d] = s / (double)Lc;
 }
 
 template <int D, int F>
@@ -649,29 +810,42 @@ hipError_t dispatch_score_F(const uint16_t* k, int B, int F, int T, int H, int T
   }
 }
 
-template <int D, int NT>
-void launch_anchor_mean_nt(const uint16_t* k, int B, int F, int T, int H, double* part,
-                           const CompressOut& out, bool q4, int Lc, hipStream_t s) {
+template <int D, int NT, int SUMS>
+void launch_anchor_mean_sums(const uint16_t* k, int B, int F, int T, int H, double* part,
+                             double* rawpart, const CompressOut& out, bool q4, int Lc,
+                             hipStream_t s) {
   const int mt = compress_mean_tokens(B, T, H);
   const dim3 grid((T + mt - 1) / mt, B);
   constexpr int W = NT / kWave;
   const size_t lds = (size_t)H * D * sizeof(double) +
                      W * (q4 ? SliceStage<D / 32, true>::BYTES : SliceStage<D / 32, false>::BYTES);
   if (q4)
-    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true, NT>), grid, dim3(NT), lds, s, k, F,
-                       T, H, mt, part, out, Lc);
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true, NT, SUMS>), grid, dim3(NT), lds, s,
+                       k, F, T, H, mt, part, rawpart, out, Lc);
   else
-    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, false, NT>), grid, dim3(NT), lds, s, k,
-                       F, T, H, mt, part, out, Lc);
+    hipLaunchKernelGGL((compress_anchor_mean_kernel<D, false, NT, SUMS>), grid, dim3(NT), lds, s,
+                       k, F, T, H, mt, part, rawpart, out, Lc);
+}
+
+// part: unit-key sums for the anchor-mean score; rawpart: anchor key sums
+// for the mean key, or null.
+template <int D, int NT>
+void launch_anchor_mean_nt(const uint16_t* k, int B, int F, int T, int H, double* part,
+                           double* rawpart, const CompressOut& out, bool q4, int Lc,
+                           hipStream_t s) {
+  if (rawpart)
+    launch_anchor_mean_sums<D, NT, 3>(k, B, F, T, H, part, rawpart, out, q4, Lc, s);
+  else
+    launch_anchor_mean_sums<D, NT, 1>(k, B, F, T, H, part, rawpart, out, q4, Lc, s);
 }
 
 template <int D>
 void launch_anchor_mean(const uint16_t* k, int B, int F, int T, int H, double* part,
-                        const CompressOut& out, bool q4, int Lc, hipStream_t s) {
+                        double* rawpart, const CompressOut& out, bool q4, int Lc, hipStream_t s) {
   if (mean_block_threads(H) == 512)
-    launch_anchor_mean_nt<D, 512>(k, B, F, T, H, part, out, q4, Lc, s);
+    launch_anchor_mean_nt<D, 512>(k, B, F, T, H, part, rawpart, out, q4, Lc, s);
   else
-    launch_anchor_mean_nt<D, 256>(k, B, F, T, H, part, out, q4, Lc, s);
+    launch_anchor_mean_nt<D, 256>(k, B, F, T, H, part, rawpart, out, q4, Lc, s);
 }
 
 }  // namespace
@@ -729,6 +903,13 @@ int compress_mean_slices(int B, int T, int H) {
   return (T + mt - 1) / mt;
 }
 
+size_t compress_anchor_lds_bytes(int H, int D, bool q4) {
+  const int W = mean_block_threads(H) / kWave;
+  const size_t stage = D == 128 ? (q4 ? SliceStage<4, true>::BYTES : SliceStage<4, false>::BYTES)
+                                : (q4 ? SliceStage<2, true>::BYTES : SliceStage<2, false>::BYTES);
+  return (size_t)H * D * sizeof(double) + W * stage;
+}
+
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4) {
   const int TT = compress_score_tile(B, T, H, q4 || mean);
   if (mean) return ((size_t)TT * (F - 1) * H + (size_t)H * (D + kAbarSkew)) * sizeof(double);
@@ -738,27 +919,57 @@ size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bo
   return score_stage_offset(TT, F, H) + W * stage;
 }
 
+int compress_key_slices(int cpr) { return (cpr + 64 * kGatherUnroll - 1) / (64 * kGatherUnroll); }
+
+// Rows per wave of the summing gather: each block writes one partial row of
+// H*D doubles, 4 / (kKsumWaves * rw) of the bytes it reads, so rw starts at 4
+// and doubles (to 32) while the grid keeps >= 1024 blocks.
+int compress_key_rw(int B, int rows, int cpr) {
+  const long long ncs = compress_key_slices(cpr);
+  int rw = 4;
+  while (rw < 32 &&
+         (long long)B * ncs * ((rows + 2 * kKsumWaves * rw - 1) / (2 * kKsumWaves * rw)) >= 1024)
+    rw *= 2;
+  return rw;
+}
+
+int compress_key_runs(int B, int rows, int cpr) {
+  const int per = kKsumWaves * compress_key_rw(B, rows, cpr);
+  return (rows + per - 1) / per;
+}
+
+int compress_key_runs_max(int B, int F, int T, int cpr) {
+  int m = 0;
+  for (int rows = 1; rows <= F * T; ++rows) m = std::max(m, compress_key_runs(B, rows, cpr));
+  return m;
+}
+
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                            int T, int H, int D, int n_keep, const CompressDst& dst,
                            int32_t* kept_idx, double* scores, bool need_scores,
-                           double* mean_part, double* abar, hipStream_t s) {
+                           double* mean_part, double* abar, const KeyMeanWs& km,
+                           hipStream_t s) {
   const bool q4 = dst.k_packed != nullptr;
   const CompressOut out{dst.k, dst.v, dst.k_packed, dst.v_packed, dst.k_scale, dst.v_scale};
   const int N = (F - 1) * T;
   const int Lc = T + n_keep;
   const int cpr = H * D / 8;
   const bool score = need_scores || (n_keep > 0 && n_keep < N);
+  const bool kmean = km.key_mean != nullptr;
   hipError_t e = hipSuccess;
+  // The anchor-mean score adds the anchor rows themselves beside their unit
+  // keys for the mean key (no extra read); otherwise the summing gather adds
+  // them, reading them again.
+  const bool araw = kmean && abar != nullptr;
   if (score) {
-    if (abar) {
-      const int ns = compress_mean_slices(B, T, H);
+    if (abar) {  // the anchor-mean kernel also writes the anchor rows
       if (D == 128)
-        launch_anchor_mean<128>(k, B, F, T, H, mean_part, out, q4, Lc, s);
+        launch_anchor_mean<128>(k, B, F, T, H, mean_part, araw ? km.araw : nullptr, out, q4, Lc, s);
       else
-        launch_anchor_mean<64>(k, B, F, T, H, mean_part, out, q4, Lc, s);
+        launch_anchor_mean<64>(k, B, F, T, H, mean_part, araw ? km.araw : nullptr, out, q4, Lc, s);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hipLaunchKernelGGL(compress_anchor_mean_final_kernel, dim3(H, B), dim3(D), 0, s,
-                         mean_part, ns, T, H, abar);
+                         mean_part, compress_mean_slices(B, T, H), T, H, abar);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int TT = compress_score_tile(B, T, H, q4 || abar != nullptr);
@@ -777,13 +988,44 @@ hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F,
                        n_keep, kept_idx, Lc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid(Lc, B, 2);
+  const int k_first = score ? T : 0;  // K rows the gather writes (the rest are anchor rows)
+  if (!kmean) {
+    dim3 grid(Lc, B, 2);
+    if (q4)
+      hipLaunchKernelGGL(compress_gather_kernel<true>, grid, dim3(kGatherBlock), 0, s, k, v,
+                         kept_idx, F * T, Lc, cpr, k_first, out, 0);
+    else
+      hipLaunchKernelGGL(compress_gather_kernel<false>, grid, dim3(kGatherBlock), 0, s, k, v,
+                         kept_idx, F * T, Lc, cpr, k_first, out, 0);
+    return hipGetLastError();
+  }
+  // Mean key: V rows by the gather; K rows by the summing gather, which
+  // copies rows from k_first on and adds rows from r_first on.
+  dim3 vgrid(Lc, B, 1);
   if (q4)
-    hipLaunchKernelGGL(compress_gather_kernel<true>, grid, dim3(kGatherBlock), 0, s, k, v,
-                       kept_idx, F * T, Lc, cpr, score ? T : 0, out);
+    hipLaunchKernelGGL(compress_gather_kernel<true>, vgrid, dim3(kGatherBlock), 0, s, k, v,
+                       kept_idx, F * T, Lc, cpr, 0, out, 1);
   else
-    hipLaunchKernelGGL(compress_gather_kernel<false>, grid, dim3(kGatherBlock), 0, s, k, v,
-                       kept_idx, F * T, Lc, cpr, score ? T : 0, out);
+    hipLaunchKernelGGL(compress_gather_kernel<false>, vgrid, dim3(kGatherBlock), 0, s, k, v,
+                       kept_idx, F * T, Lc, cpr, 0, out, 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int r_first = araw ? T : 0;
+  const int rows = Lc - r_first;
+  const int rw = compress_key_rw(B, rows, cpr);
+  const int nruns = compress_key_runs(B, rows, cpr);
+  if (nruns > 0) {
+    dim3 kgrid(nruns, compress_key_slices(cpr), B);
+    if (q4)
+      hipLaunchKernelGGL(compress_gather_ksum_kernel<true>, kgrid, dim3(kKsumBlock), 0, s, k,
+                         kept_idx, F * T, Lc, cpr, r_first, rw, k_first, out, km.ksum);
+    else
+      hipLaunchKernelGGL(compress_gather_ksum_kernel<false>, kgrid, dim3(kKsumBlock), 0, s, k,
+                         kept_idx, F * T, Lc, cpr, r_first, rw, k_first, out, km.ksum);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(compress_key_mean_final_kernel, dim3(H, B), dim3(D * kFinalGroups), 0, s,
+                     km.araw, araw ? compress_mean_slices(B, T, H) : 0, km.ksum, nruns, Lc, H,
+                     km.key_mean);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ constexpr int64_t kMaxWindowRows = (1LL << 26) - 1;  // one 64-lane block per ro
 int compress_score_tile(int B, int T, int H, bool grow);
 int compress_mean_slices(int B, int T, int H);  // anchor-token slices of the anchor-mean sums
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4);
+size_t compress_anchor_lds_bytes(int H, int D, bool q4);  // the anchor-mean kernel
 // Destination of the compressed rows: bf16 rows (k, v) when k_packed is
 // null, else int4 codes (k_packed, v_packed: [B][Lc][H][D/2]) with bf16 group
 // scales (k_scale, v_scale: [B][Lc][H][D/32]).
@@ -26,13 +27,28 @@ struct CompressDst {
   uint16_t* k_scale;
   uint16_t* v_scale;
 };
+// The mean key of each compressed unit (float64 [B][H][D]), when key_mean is
+// given: araw [B][H][slices][D] holds the anchor-row sums of the anchor-mean
+// score's kernel (slices as for that score; used with the anchor-mean score
+// only), ksum [B][runs][H*D] the sums of the summing gather's runs.
+struct KeyMeanWs {
+  double* key_mean;
+  double* araw;
+  double* ksum;
+};
+// Column slices and runs of the summing gather for `rows` K rows per unit,
+// and the most runs any keep ratio and score mode give (rows <= F*T): ksum
+// holds B * compress_key_runs_max * H*D doubles.
+int compress_key_slices(int cpr);
+int compress_key_runs(int B, int rows, int cpr);
+int compress_key_runs_max(int B, int F, int T, int cpr);
 // mean_part [B][H][slices][D] and abar [B][H][D] (float64) are used, and must
 // be given, for the anchor-mean score only; abar == nullptr selects the
 // position-aligned score.
 hipError_t compress_launch(const uint16_t* k, const uint16_t* v, int B, int F, int T,
                            int H, int D, int n_keep, const CompressDst& dst,
                            int32_t* kept_idx, double* scores, bool need_scores,
-                           double* mean_part, double* abar, hipStream_t s);
+                           double* mean_part, double* abar, const KeyMeanWs& km, hipStream_t s);
 
 // The compression workspace of callers that cannot allocate: a file-scope
 // device array of compress_scratch_bytes() bytes per GPU. compress_scratch()

@@ -78,15 +78,16 @@ def _sig(name, res, args):
 _abi_version = _sig("wkv_abi_version", _I32, [])
 _last_error = _sig("wkv_last_error", C.c_char_p, [])
 _keep_count = _sig("wkv_keep_count", _I32, [_I32, _I32, _F])
-_compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 6)
+_compress_ws = _sig("wkv_compress_workspace_bytes", _SZ, [_I32] * 7)
 _score_tile = _sig("wkv_compress_score_tile", _I32, [_I32] * 5)
 _compress = _sig("wkv_compress_chunk", C.c_int,
-                 [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _SZ, _P])
+                 [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _SZ,
+                  _P])
 _compress_na = _sig("wkv_compress_chunk_noalloc", C.c_int,
                     [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P])
 _compress4 = _sig("wkv_compress_chunk_int4", C.c_int,
                   [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P,
-                   _SZ, _P])
+                   _P, _SZ, _P])
 _pose_extrap = _sig("wkv_pose_extrapolate", wkv_pose, [wkv_pose, wkv_pose])
 _pose_host = _sig("wkv_pose_topk_host", C.c_int,
                   [_P, _I32, C.POINTER(wkv_pose), _I32, _I32, _P, _P])
@@ -241,8 +242,8 @@ def _score_mode(mode) -> int:
 
 
 def wkv_compress_workspace_bytes(B: int, F: int, T: int, H: int, D: int,
-                                 score_mode="position") -> int:
-    return int(_compress_ws(B, F, T, H, D, _score_mode(score_mode)))
+                                 score_mode="position", key_mean: bool = False) -> int:
+    return int(_compress_ws(B, F, T, H, D, _score_mode(score_mode), 1 if key_mean else 0))
 
 
 def wkv_compress_score_tile(B: int, T: int, H: int, score_mode="position",
@@ -258,9 +259,11 @@ def wkv_attention_workspace_bytes(Nq: int, Nk: int, H: int, D: int) -> int:
 def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
                        k_out=None, v_out=None, kept_idx=None, scores=None,
                        want_scores: bool = False, ws=None, stream=None,
-                       score_mode="position"):
+                       score_mode="position", key_mean=None):
     """World Compression of B units. k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]).
     score_mode: "position" / "anchor_mean" (or the WKV_SCORE_* value).
+    key_mean: optional float64 [B, H, D] (or [H, D]) filled with the mean of
+    each unit's compressed K rows.
     Returns (k_out, v_out, kept_idx, scores-or-None)."""
     _bits(k, "k"), _bits(v, "v")
     if k.dim() not in (3, 4) or tuple(v.shape) != tuple(k.shape):
@@ -279,8 +282,10 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     v_out = _unit_out(v_out, "v_out", _BF16, (B, Lc, H, D), squeeze)
     kept_idx = _unit_out(kept_idx, "kept_idx", _I32, (B, Lc), squeeze)
     scores = _unit_out(scores, "scores", (torch.float64,), (B, N), squeeze)
+    key_mean = _unit_out(key_mean, "key_mean", (torch.float64,), (B, H, D), squeeze)
     dev = _on_device(("k", k), ("v", v), ("k_out", k_out), ("v_out", v_out),
-                     ("kept_idx", kept_idx), ("scores", scores), ("ws", ws))
+                     ("kept_idx", kept_idx), ("scores", scores), ("key_mean", key_mean),
+                     ("ws", ws))
     if k_out is None:
         k_out = torch.empty((B, Lc, H, D), dtype=k.dtype, device=dev)
     if v_out is None:
@@ -290,11 +295,11 @@ def wkv_compress_chunk(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: floa
     if scores is None and want_scores:
         scores = torch.empty((B, N), dtype=torch.float64, device=dev)
     if ws is None:
-        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
+        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode, key_mean is not None)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     st = _compress(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
-                   _ptr(k_out), _ptr(v_out),
-                   _ptr(kept_idx), _ptr(scores), _ptr(ws), _ws_bytes(ws), _stream(stream))
+                   _ptr(k_out), _ptr(v_out), _ptr(kept_idx), _ptr(scores), _ptr(key_mean),
+                   _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check("wkv_compress_chunk", st)
     if squeeze:
         k_out, v_out, kept_idx = k_out[0], v_out[0], kept_idx[0]
@@ -334,11 +339,12 @@ def wkv_compress_chunk_noalloc(k: torch.Tensor, v: torch.Tensor, F: int, T: int,
 def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r: float,
                             k_packed=None, v_packed=None, k_scale=None, v_scale=None,
                             kept_idx=None, scores=None, want_scores: bool = False, ws=None,
-                            stream=None, score_mode="position"):
+                            stream=None, score_mode="position", key_mean=None):
     """World Compression of B units, stored as int4 groups with bf16 scales.
-    k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]). Returns (k_packed, v_packed,
-    k_scale, v_scale, kept_idx, scores-or-None): uint8 [B, Lc, H, D/2] and
-    bf16 [B, Lc, H, D/32]."""
+    k, v: bf16 [B, F*T, H, D] (or [F*T, H, D]). key_mean: optional float64
+    [B, H, D] (or [H, D]) filled with the mean of each unit's retained K rows
+    before encoding. Returns (k_packed, v_packed, k_scale, v_scale, kept_idx,
+    scores-or-None): uint8 [B, Lc, H, D/2] and bf16 [B, Lc, H, D/32]."""
     _bits(k, "k"), _bits(v, "v")
     if k.dim() not in (3, 4) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"k, v: expected equal [B, F*T, H, D] shapes, got {tuple(k.shape)}, "
@@ -359,9 +365,10 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
     v_scale = _unit_out(v_scale, "v_scale", _BF16, (B, Lc, H, D // 32), squeeze)
     kept_idx = _unit_out(kept_idx, "kept_idx", _I32, (B, Lc), squeeze)
     scores = _unit_out(scores, "scores", (torch.float64,), (B, N), squeeze)
+    key_mean = _unit_out(key_mean, "key_mean", (torch.float64,), (B, H, D), squeeze)
     dev = _on_device(("k", k), ("v", v), ("k_packed", k_packed), ("v_packed", v_packed),
                      ("k_scale", k_scale), ("v_scale", v_scale), ("kept_idx", kept_idx),
-                     ("scores", scores), ("ws", ws))
+                     ("scores", scores), ("key_mean", key_mean), ("ws", ws))
     if k_packed is None:
         k_packed = torch.empty((B, Lc, H, D // 2), dtype=torch.uint8, device=dev)
     if v_packed is None:
@@ -375,11 +382,12 @@ def wkv_compress_chunk_int4(k: torch.Tensor, v: torch.Tensor, F: int, T: int, r:
     if scores is None and want_scores:
         scores = torch.empty((B, N), dtype=torch.float64, device=dev)
     if ws is None:
-        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
+        nb = wkv_compress_workspace_bytes(B, F, T, H, D, score_mode, key_mean is not None)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     st = _compress4(_ptr(k), _ptr(v), B, F, T, H, D, r, _score_mode(score_mode),
                     _ptr(k_packed), _ptr(v_packed), _ptr(k_scale), _ptr(v_scale),
-                    _ptr(kept_idx), _ptr(scores), _ptr(ws), _ws_bytes(ws), _stream(stream))
+                    _ptr(kept_idx), _ptr(scores), _ptr(key_mean), _ptr(ws), _ws_bytes(ws),
+                    _stream(stream))
     _check("wkv_compress_chunk_int4", st)
     outs = [k_packed, v_packed, k_scale, v_scale, kept_idx]
     if squeeze:

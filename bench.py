@@ -390,13 +390,38 @@ def main():
             t_mk = statistics.fmean(e[0].elapsed_time(e[1]) for e in qev)
             t_mq = statistics.fmean(e[1].elapsed_time(e[2]) for e in qev)
             t_tk = statistics.fmean(e[2].elapsed_time(e[3]) for e in qev)
+            # The mean key as a by-product of compression: the same call with
+            # and without its key_mean output, alternating
+            kws = torch.empty(max(w.wkv_compress_workspace_bytes(1, F, T, H, D, a.score_mode,
+                                                                 True), 16),
+                              dtype=torch.uint8, device=dev)
+            kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
+            for i in range(25):
+                s = sets[i % len(sets)]
+                e = kev[i - 5] if i >= 5 else None
+                if e:
+                    e[0].record()
+                w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                     kept_idx=s["kidx"], ws=kws, score_mode=a.score_mode)
+                if e:
+                    e[1].record()
+                w.wkv_compress_chunk(s["ek"], s["ev"], F, T, r, k_out=s["ko"], v_out=s["vo"],
+                                     kept_idx=s["kidx"], ws=kws, score_mode=a.score_mode,
+                                     key_mean=kmo[0])
+                if e:
+                    e[2].record()
+            torch.cuda.synchronize()
+            t_c0 = statistics.fmean(e[0].elapsed_time(e[1]) for e in kev)
+            t_c1 = statistics.fmean(e[1].elapsed_time(e[2]) for e in kev)
             R = H * D * 2
             qr = {"mean_key_us": round(t_mk * 1e3, 2),
                   "mean_key_GBps": round(Lc * R / (t_mk * 1e-3) / 1e9, 1),
+                  "compress_us": round(t_c0 * 1e3, 2),
+                  "compress_with_mean_key_us": round(t_c1 * 1e3, 2),
                   "mean_query_us": round(t_mq * 1e3, 2),
                   "mean_query_GBps": round(Nq * R / (t_mq * 1e-3) / 1e9, 1),
                   "query_topk_us": round(t_tk * 1e3, 2)}
-            del km_bank, mws
+            del km_bank, mws, kws
 
         # ---- the window read in place (bf16 banks): the same serial steps
         # with wkv_chunk_attention_window in place of assembly + attention,
@@ -601,10 +626,11 @@ def _compress_call(w, kin, vin, F, T, r, out, ws, score_mode):
     if "kp" in out:
         w.wkv_compress_chunk_int4(kin, vin, F, T, r, k_packed=out["kp"], v_packed=out["vp"],
                                   k_scale=out["ks"], v_scale=out["vs"], kept_idx=out["ki"],
-                                  ws=ws, score_mode=score_mode)
+                                  ws=ws, score_mode=score_mode, key_mean=out.get("km"))
     else:
         w.wkv_compress_chunk(kin, vin, F, T, r, k_out=out["ko"], v_out=out["vo"],
-                             kept_idx=out["ki"], ws=ws, score_mode=score_mode)
+                             kept_idx=out["ki"], ws=ws, score_mode=score_mode,
+                             key_mean=out.get("km"))
 
 
 def _time_compress(torch, w, kin, vin, F, T, r, out, ws, score_mode, calls, warm, reps):
@@ -630,8 +656,10 @@ def compress_batches(a, torch, w, S, dev):
     """Batched World Compression beside the step: one call over 300 resident
     units of the 1.3B-class chunk shape (3x880 tokens x 12 heads x d128, 70%
     redundancy; 4.9 GB of keys and values, far past the last-level cache),
-    bf16 and int4 stores at r = 0.25 and 0.5, position score; GB/s of
-    algorithmic bytes from HIP events on the launch stream."""
+    bf16 and int4 stores at r = 0.25 and 0.5, position score, each also with
+    the mean key of every unit written beside it; GB/s of algorithmic bytes
+    (the mean key's 12 KiB per unit aside) from HIP events on the launch
+    stream."""
     c = SWEEP
     H, D, T, F, B = c["H"], c["D"], c["T"], c["F"], c["batch"]
     cells = {}
@@ -641,19 +669,23 @@ def compress_batches(a, torch, w, S, dev):
         vin = torch.empty_like(kin)
         for u in range(B):
             kin[u], vin[u] = S.chunk_kv(3, u, 1, F, T, H, D, p_red=0.7, device=dev)
-        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T, H, D, "position"), 16),
-                         dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(w.wkv_compress_workspace_bytes(B, F, T, H, D, "position", True),
+                             16), dtype=torch.uint8, device=dev)
         for store in ("bf16", "int4"):
             for r in (0.25, 0.5):
                 n_keep = w.wkv_keep_count(F, T, r)
                 Lc = T + n_keep
                 out = _compress_outputs(torch, B, Lc, H, D, store, dev)
-                ms = _time_compress(torch, w, kin, vin, F, T, r, out, ws, "position", 1, 2, 7)
-                nbytes = compress_bytes(c, Lc, n_keep, store == "int4") * B
-                gbps = nbytes / (ms * 1e-3) / 1e9
-                cells[f"{store} r={r}"] = {"ms": round(ms, 4), "GB": round(nbytes / 1e9, 3),
-                                           "GBps": round(gbps, 1),
-                                           "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+                for km in (False, True):
+                    out["km"] = (torch.empty((B, H, D), dtype=torch.float64, device=dev)
+                                 if km else None)
+                    ms = _time_compress(torch, w, kin, vin, F, T, r, out, ws, "position", 1, 2,
+                                        7)
+                    nbytes = compress_bytes(c, Lc, n_keep, store == "int4") * B
+                    gbps = nbytes / (ms * 1e-3) / 1e9
+                    cells[f"{store} r={r}" + (" +mean key" if km else "")] = {
+                        "ms": round(ms, 4), "GB": round(nbytes / 1e9, 3), "GBps": round(gbps, 1),
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4)}
                 del out
         del kin, vin, ws
     torch.cuda.synchronize()
@@ -937,7 +969,7 @@ def tier_bench(a, torch, w, S, dev):
     rec_ = (w.wkv_segment * max(nrec, 1))(*[w._seg(p_) for p_ in segs[1:1 + nrec]])
     stg_b, bank_b = w._bank_struct(staging), w._bank_struct(bank)
     comp_args = (P(ck.data_ptr()), P(cv.data_ptr()), 1, F, T, H, D, float(r), 0,
-                 P(ko.data_ptr()), P(vo.data_ptr()), P(kidx.data_ptr()), None,
+                 P(ko.data_ptr()), P(vo.data_ptr()), P(kidx.data_ptr()), None, None,
                  P(cws.data_ptr()), cws.numel(), cs_h)
     attn_args = [(P(qs[j].data_ptr()), P(wk.data_ptr()), P(wv.data_ptr()), Nq, Nk, H, D, 0.0,
                   P(out.data_ptr()), None, P(aws.data_ptr()), aws.numel(), cs_h)

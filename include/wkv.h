@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define WKV_ABI_VERSION 2
+#define WKV_ABI_VERSION 3
 
 typedef void* wkv_stream_t; /* hipStream_t */
 
@@ -135,11 +135,13 @@ int32_t wkv_keep_count(int32_t F, int32_t T, float r);
 
 enum { WKV_SCORE_POSITION = 0, WKV_SCORE_ANCHOR_MEAN = 1 };
 
-/* [host] Workspace bytes wkv_compress_chunk needs for B units with the given
- * score mode (an upper bound: a call that is given its scores output, or
- * that needs no score at r = 0 or 1, uses less). 0 for invalid arguments. */
+/* [host] Workspace bytes wkv_compress_chunk (or _int4) needs for B units
+ * with the given score mode, with key_mean != 0 when the call is given a
+ * key_mean output (an upper bound for every keep ratio: a call that is given
+ * its scores output, or that needs no score at r = 0 or 1, uses less). 0 for
+ * invalid arguments. */
 size_t wkv_compress_workspace_bytes(int32_t B, int32_t F, int32_t T, int32_t H,
-                                    int32_t D, int32_t score_mode);
+                                    int32_t D, int32_t score_mode, int32_t key_mean);
 
 /* [host] Diagnostic: anchor-frame tokens each block of the compression score
  * kernel covers for a call on B units of T tokens and H heads with the given
@@ -159,14 +161,23 @@ int32_t wkv_compress_score_tile(int32_t B, int32_t T, int32_t H, int32_t score_m
  *                                             every output row, ascending
  *   score_mode WKV_SCORE_POSITION or WKV_SCORE_ANCHOR_MEAN
  *   scores     double [B][(F-1)*T] or NULL    optional output
- *   ws         >= wkv_compress_workspace_bytes(B, F, T, H, D, score_mode)
- *              bytes (may be NULL when that is 0)
+ *   key_mean   double [B][H][D] or NULL       optional output: the mean key of
+ *                                             each compressed unit, the
+ *                                             float64 mean of its Lc K rows
+ *                                             per (head, dim), as query-based
+ *                                             retrieval scores stored chunks
+ *                                             (wkv_query_topk); equal to
+ *                                             wkv_mean_rows of k_out up to
+ *                                             the order of the float64 sums;
+ *                                             bitwise reproducible
+ *   ws         >= wkv_compress_workspace_bytes(B, F, T, H, D, score_mode,
+ *              key_mean != NULL) bytes (may be NULL when that is 0)
  * Limits: 1 <= B <= 65535; 2 <= F <= 4; 1 <= T; (F-1)*T <= 8192; 0 <= r <= 1.
  * Errors: WKV_ERR_UNSUPPORTED for an unknown score_mode. */
 wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
                               int32_t F, int32_t T, int32_t H, int32_t D,
                               float r, int32_t score_mode, uint16_t* k_out, uint16_t* v_out,
-                              int32_t* kept_idx, double* scores, void* ws,
+                              int32_t* kept_idx, double* scores, double* key_mean, void* ws,
                               size_t ws_bytes, wkv_stream_t stream);
 
 /* wkv_compress_chunk without a workspace argument, for callers that cannot
@@ -175,8 +186,9 @@ wkv_status wkv_compress_chunk(const uint16_t* k, const uint16_t* v, int32_t B,
  * of 64 MiB that every GPU the library runs on holds until the process ends;
  * its address on a device is resolved on the first call on that device
  * (make that first call outside graph capture). The call allocates nothing.
- * A call whose workspace (wkv_compress_workspace_bytes, less the scores when
- * given) exceeds 64 MiB is refused with WKV_ERR_WORKSPACE. Every call on one
+ * A call whose workspace (wkv_compress_workspace_bytes with key_mean = 0,
+ * less the scores when given) exceeds 64 MiB is refused with
+ * WKV_ERR_WORKSPACE. It has no key_mean output. Every call on one
  * GPU shares that GPU's array, which keeps the last call's contents: calls
  * that overlap on one GPU (on different streams, or concurrently enqueued by
  * other threads) race and must be ordered by the caller. Arguments, outputs,
@@ -199,13 +211,17 @@ wkv_status wkv_compress_chunk_noalloc(const uint16_t* k, const uint16_t* v, int3
  *   v_packed   uint8 [B][Lc][H][D/2]           outputs
  *   k_scale,
  *   v_scale    bf16  [B][Lc][H][D/32]          outputs
+ *   key_mean   double [B][H][D] or NULL        optional output: the mean of the
+ *                                              unit's retained K rows as read
+ *                                              (before encoding), exactly as
+ *                                              wkv_compress_chunk gives it
  * Other arguments, limits and errors as wkv_compress_chunk. Inputs must be
  * finite: the codes of a group holding an Inf or NaN are unspecified. */
 wkv_status wkv_compress_chunk_int4(const uint16_t* k, const uint16_t* v, int32_t B,
                                    int32_t F, int32_t T, int32_t H, int32_t D, float r,
                                    int32_t score_mode, uint8_t* k_packed, uint8_t* v_packed,
                                    uint16_t* k_scale, uint16_t* v_scale, int32_t* kept_idx,
-                                   double* scores, void* ws, size_t ws_bytes,
+                                   double* scores, double* key_mean, void* ws, size_t ws_bytes,
                                    wkv_stream_t stream);
 
 /* ------------------------------------------------------------------------

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(w):
 
 
 def test_abi_version_and_keep_count(w):
-    assert w.wkv_abi_version() == 2
+    assert w.wkv_abi_version() == 3
     assert w.wkv_keep_count(3, 880, 0.5) == 880
     assert w.wkv_keep_count(3, 880, 0.25) == 440
     assert w.wkv_keep_count(3, 1560, 0.25) == 780
@@ -78,12 +78,12 @@ def st(fn, *args):
 
 def test_compress_validation(w):
     f = w._compress
-    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, None, A, 1 << 20, None]
+    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, None, None, A, 1 << 20, None]
 
     def call(**kw):
         a = list(ok)
-        names = ["k", "v", "B", "F", "T", "H", "D", "r", "mode", "ko", "vo", "ki", "sc", "ws",
-                 "wsb", "s"]
+        names = ["k", "v", "B", "F", "T", "H", "D", "r", "mode", "ko", "vo", "ki", "sc", "km",
+                 "ws", "wsb", "s"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return f(*a)
@@ -111,6 +111,11 @@ def test_compress_validation(w):
     # anchor-mean needs room for its partial sums even when scores are given
     assert call(mode=1, sc=A, ws=None, wsb=0) == 6
     assert call(mode=1, wsb=w.wkv_compress_workspace_bytes(1, 3, 64, 2, 64, "anchor_mean") - 1) == 6
+    # the mean key: misaligned output, and a workspace sized without its sums
+    assert call(km=MIS) == 5
+    assert call(km=A, wsb=w.wkv_compress_workspace_bytes(1, 3, 64, 2, 64)) == 6
+    assert call(km=A, mode=1, ws=A,
+                wsb=w.wkv_compress_workspace_bytes(1, 3, 64, 2, 64, "anchor_mean", True) - 1) == 6
 
 
 def test_pose_validation(w):
@@ -171,9 +176,9 @@ def test_attention_validation(w):
 
 def test_compress_int4_validation(w):
     f = w._compress4
-    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, A, A, None, A, 1 << 20, None]
+    ok = [A, A, 1, 3, 64, 2, 64, 0.5, 0, A, A, A, A, A, None, None, A, 1 << 20, None]
     names = ["k", "v", "B", "F", "T", "H", "D", "r", "mode", "kp", "vp", "ks", "vs", "ki", "sc",
-             "ws", "wsb", "s"]
+             "km", "ws", "wsb", "s"]
 
     def call(**kw):
         a = list(ok)
