@@ -43,20 +43,25 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # Workloads: heads x head dim, tokens per frame, frames per chunk, keep ratio,
-# stored chunks, retrieved k, recent chunks, denoising steps, int4 bank.
+# stored chunks, retrieved k, recent chunks, denoising steps, int4 bank, and
+# the streams the timed step uses: 2 runs step i+1's compression and
+# retrieval beside step i's attention; 1 runs every call in order. The
+# 14B-class step is 98 % attention, whose 0.9 ms blocks fill the chip in
+# under three rounds: work beside it delays blocks into a later round, which
+# cost 0.4-0.7 ms per step on three boxes, against 0.06 ms of work hidden.
 CONFIGS = {
-    "tiny": dict(H=2, D=64, T=64, F=3, r=0.5, M=8, k=2, n_recent=1, S=1, int4=False,
+    "tiny": dict(H=2, D=64, T=64, F=3, r=0.5, M=8, k=2, n_recent=1, S=1, int4=False, streams=2,
                  name="tiny: 2 heads x d64, 3x64-token chunks, 8 stored chunks, "
                       "window sink + 2 retrieved (r=0.5) + 1 recent + current"),
-    "1.3b": dict(H=12, D=128, T=880, F=3, r=0.5, M=20, k=3, n_recent=2, S=1, int4=False,
+    "1.3b": dict(H=12, D=128, T=880, F=3, r=0.5, M=20, k=3, n_recent=2, S=1, int4=False, streams=2,
                  name="1.3B-class single layer: 12 heads x d128, 3x880-token chunks, "
                       "20 stored chunks, window sink + 3 retrieved (r=0.5) + 2 recent "
                       "+ current"),
-    "14b": dict(H=40, D=128, T=1560, F=3, r=0.25, M=120, k=6, n_recent=2, S=4, int4=False,
+    "14b": dict(H=40, D=128, T=1560, F=3, r=0.25, M=120, k=6, n_recent=2, S=4, int4=False, streams=1,
                 name="14B-class single layer: 40 heads x d128, 3x1560-token chunks, "
                      "120 stored chunks, window sink + 6 retrieved (r=0.25) + 2 recent "
                      "+ current, 4 denoising steps"),
-    "int4": dict(H=12, D=128, T=880, F=3, r=0.5, M=1000, k=4, n_recent=2, S=1, int4=True,
+    "int4": dict(H=12, D=128, T=880, F=3, r=0.5, M=1000, k=4, n_recent=2, S=1, int4=True, streams=2,
                  name="long-rollout int4 store: 12 heads x d128, 3x880-token chunks, "
                       "1000 stored int4 chunks (r=0.5, g32 bf16 scales), extrapolated "
                       "query pose, window sink + 4 retrieved + 2 recent + current"),
@@ -88,6 +93,8 @@ def parse():
     ap.add_argument("--store", default="bf16", choices=["bf16", "int4"],
                     help="format of the compressed rows in the sweep")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--streams", type=int, default=None, choices=[1, 2],
+                    help="streams of the timed step (default: the workload's)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows per oracle attention call in the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -298,11 +305,11 @@ def main():
         run_pipelined(max(2, a.warmup))
         torch.cuda.synchronize()
 
-        # ---- timed region: wall clock over exactly K pipelined steps (no
-        # cyclic-GC pass inside it); the first step's compression and
-        # retrieval are inside it too. The serial run of the same steps
-        # goes first.
-        # the same K steps on one stream, one after another (reported beside)
+        # ---- timed regions: wall clock over exactly K steps (no cyclic-GC
+        # pass inside either), first on one stream, one call after another,
+        # then pipelined on two (the first step's compression and retrieval
+        # inside it). The workload's schedule gives the value; the other is
+        # reported beside it.
         torch.cuda.synchronize()
         t2 = time.perf_counter()
         for i in range(a.steps):
@@ -315,8 +322,10 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         gc.enable()
-        wall = t1 - t0
+        wall_pipe = t1 - t0
         wall_serial = t3 - t2
+        nstreams = a.streams or c["streams"]
+        wall = wall_serial if nstreams == 1 else wall_pipe
 
         # ---- per-call durations, from HIP events on the launch stream
         nev = 4 + 2 * nsteps
@@ -546,10 +555,12 @@ def main():
                    "stored_chunks": M, "retrieved": k, "window_keys": Nk, "queries": Nq,
                    "denoise_steps": nsteps, "int4_bank": c["int4"], "parallelism": "none",
                    "input_sets": a.sets,
-                   "streams": "2 (compression and retrieval of step i+1 beside step i's "
-                              "attention)"},
+                   "streams": ("1 (every call in order)" if nstreams == 1 else
+                               "2 (compression and retrieval of step i+1 beside step i's "
+                               "attention)")},
         "breakdown": {
             "serial_ms_per_step": round(wall_serial / a.steps * 1e3, 4),
+            "pipelined_ms_per_step": round(wall_pipe / a.steps * 1e3, 4),
             "compress_us": round(comp_ms * 1e3, 2),
             "compress_GBps": round(comp_b / (comp_ms * 1e-3) / 1e9, 1),
             "compress_bytes": comp_b,
