@@ -41,6 +41,16 @@ def test_compress_refusals():
         w.wkv_compress_chunk_int4(k, v, 3, 8, 0.5, kept_idx=torch.zeros(2, 12, dtype=torch.int64))
     with pytest.raises(ValueError, match="CUDA"):
         w.wkv_compress_chunk_int4(k, v, 3, 8, 0.5)
+    # the mean key: float64 [B, H, D]
+    with pytest.raises(TypeError, match="float64"):
+        w.wkv_compress_chunk(k, v, 3, 8, 0.5, key_mean=torch.zeros(2, 2, 64))
+    with pytest.raises(ValueError, match="key_mean: shape"):
+        w.wkv_compress_chunk(k, v, 3, 8, 0.5, key_mean=torch.zeros(2, 3, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="key_mean: shape"):
+        w.wkv_compress_chunk_int4(k, v, 3, 8, 0.5,
+                                  key_mean=torch.zeros(2, 2, 32, dtype=torch.float64))
+    with pytest.raises(ValueError, match="CUDA"):
+        w.wkv_compress_chunk(k, v, 3, 8, 0.5, key_mean=torch.zeros(2, 2, 64, dtype=torch.float64))
 
 
 def test_attention_refusals():
