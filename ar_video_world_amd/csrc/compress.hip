@@ -119,16 +119,26 @@ __device__ __forceinline__ uint32_t int4_encode_quad(const uint4& x, uint16_t* s
     // against exact rounding for all bf16 pairs with |x / sc| <= 7.02). A
     // scale so small that 1/sc overflows, or infinite, takes the division.
     // For finite groups |x / sc| <= 7 / (1 - 2^-9) < 7.5, so every code is in
-    // [-7, 7]. Adding 1.5 * 2^23 rounds k + r*inv half-to-even to an integer
-    // and leaves it, in two's complement, in the low mantissa bits.
+    // [-7, 7]. Adding 1.5 * 2^23 + 8 rounds k + r*inv half-to-even to an
+    // integer (the spacing of floats there is 1) and leaves code + 8, in
+    // [1, 15], in the low mantissa bits with bits 4..21 clear. So two codes
+    // pack into a byte with one shift-or, four bytes into a word with three
+    // byte permutes, and flipping bit 3 of every nibble turns code + 8 into
+    // the code's two's complement.
     const float inv = __fdiv_rn(1.0f, sc);
     if (inv < 3.0e38f && inv > 0.f) {
+      uint32_t t[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float k = rintf(v[e] * inv);
-        const float t = fmaf(fmaf(-k, sc, v[e]), inv, k) + 12582912.0f;
-        out |= (__float_as_uint(t) & 0xFu) << (4 * e);
+        t[e] = __float_as_uint(fmaf(fmaf(-k, sc, v[e]), inv, k) + 12582920.0f);
       }
+      uint32_t pb[4];  // byte 0 of each: codes 2j (low nibble) and 2j + 1
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[j] = (t[2 * j + 1] << 4) | t[2 * j];
+      const uint32_t lo = __builtin_amdgcn_perm(pb[1], pb[0], 0x0C0C0400u);  // [pb0.b0, pb1.b0, 0, 0]
+      const uint32_t hi = __builtin_amdgcn_perm(pb[3], pb[2], 0x04000C0Cu);  // [0, 0, pb2.b0, pb3.b0]
+      out = (lo | hi) ^ 0x88888888u;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {

@@ -5,11 +5,13 @@ definitions:
 
 * RN32(m / 7) == fma(fma(-y0, 7, m), RN32(1/7), y0) with y0 = RN32(m * RN32(1/7)),
   for every positive finite bf16 m (subnormals included);
-* the low nibble of RN32(fma(fma(-k, s, x), inv, k) + 1.5 * 2^23), with
-  k = rint(RN32(x * inv)) and inv = RN32(1 / s), is the round-half-even
-  integer of the exact x / s in two's complement, for
-  every bf16 x and bf16 scale s with |x / s| <= 7.02 (the largest quotient
-  an encoded group can hold is 7 / (1 - 2^-9)).
+* t = RN32(fma(fma(-k, s, x), inv, k) + 1.5 * 2^23 + 8), with
+  k = rint(RN32(x * inv)) and inv = RN32(1 / s), holds code + 8 in its low
+  nibble and zeros in bits 4..7, where code is the round-half-even integer of
+  the exact x / s, for every bf16 x and bf16 scale s with |x / s| <= 7.02
+  (the largest quotient an encoded group can hold is 7 / (1 - 2^-9)). The
+  kernel packs those bytes unmasked and flips bit 3 of every nibble, which
+  gives the code's two's complement.
 
 The float32 fused multiply-adds are emulated in float64, where each product
 and sum below is exact (at most 48 significant bits, or a difference of two
@@ -72,9 +74,11 @@ def _check_codes(sbits):
     k = np.rint((X * inv).astype(F32))
     r = (X.astype(F64) - k.astype(F64) * S.astype(F64)).astype(F32)
     y = (r.astype(F64) * inv.astype(F64) + k.astype(F64)).astype(F32)
-    t = (y + F32(12582912.0)).astype(F32)          # the kernel's rounding add
-    nib = (t.view(np.uint32) & 0xF).astype(np.int64)
-    q = np.where(nib >= 8, nib - 16, nib)          # two's complement of the low nibble
+    t = (y + F32(12582920.0)).astype(F32)          # the kernel's rounding add
+    tb = t.view(np.uint32)
+    assert not np.any(tb & 0xF0), "bits 4..7 of a rounded code are set"
+    nib = ((tb & 0xF) ^ 8).astype(np.int64)        # bit 3 flipped: two's complement
+    q = np.where(nib >= 8, nib - 16, nib)
     want = _rne_quotient(X, S)
     bad = np.nonzero(q != want)[0]
     assert bad.size == 0, (X[bad[:5]], S[bad[:5]], q[bad[:5]], want[bad[:5]])
