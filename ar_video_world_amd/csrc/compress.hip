@@ -228,6 +228,16 @@ __device__ __forceinline__ void stage_store(const uint4 (&a)[NLD], bool active, 
   __builtin_amdgcn_wave_barrier();
 }
 
+// The anchor-mean kernel's per-head sums sit D + 1 doubles apart, so the
+// quads writing them in one instruction (different heads, 64 bytes apart
+// within a head) spread over the LDS banks two lanes deep instead of
+// meeting on one bank per head (a stride of D doubles is a whole number of
+// bank rounds: 6.6 conflict cycles per LDS instruction on 300 units of
+// 3 x 880 x 12 x 128). The slice stages follow from the next 16 bytes.
+__host__ __device__ inline size_t anchor_stage_offset(int H, int D) {
+  return ((size_t)H * (D + 1) * sizeof(double) + 15) / 16 * 16;
+}
+
 // Anchor-mean blocks: 256 lanes, or 512 when 256 would leave over an eighth
 // more of the quads idle (40 heads: 40 of 64 quads against 120 of 128) or
 // cannot hold one quad per head.
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
   constexpr int E = NLD * 8;  // elements per lane
   constexpr bool UNIT = SUMS & 1, RAW = SUMS & 2;
   constexpr int NQ = NT / kLanesPerPair;
-  extern __shared__ double red[];  // [H][D], then the waves' slice stages
+  extern __shared__ double red[];  // [H][D + 1], then the waves' slice stages
   const int sl = blockIdx.x, b = blockIdx.y;
   const int P = NQ / H;  // tokens per pass (H <= NQ)
   const int j0 = sl * mt;
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
   // Quads past the last full head set idle. Passes run together over the
   // block (pass k takes tokens kP .. kP+P-1, all heads: P*H consecutive
   // (row, head) slices), so each wave's anchor slices leave through its stage.
-  uint8_t* stage = reinterpret_cast<uint8_t*>(red + (size_t)H * D) +
+  uint8_t* stage = reinterpret_cast<uint8_t*>(red) + anchor_stage_offset(H, D) +
                    (tid / kWave) * SliceStage<NLD, Q4>::BYTES;
   const int qw = q % 16;
   const int wq0 = q - qw;  // the wave's first quad
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
         for (int i = 0; i < NLD; ++i)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            double* cell = red + h * D + i * 32 + sub * 8 + e;
+            double* cell = red + h * (D + 1) + i * 32 + sub * 8 + e;
             *cell = (r == 0) ? v[i * 8 + e] : *cell + v[i * 8 + e];
           }
       }
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(NT) void compress_anchor_mean_kernel(
     double* dst = out_part + (size_t)b * HD * gridDim.x;
     for (int i = tid; i < (int)HD; i += NT) {
       const int hh = i / D, d = i - hh * D;
-      dst[((size_t)hh * gridDim.x + sl) * D + d] = red[i];
+      dst[((size_t)hh * gridDim.x + sl) * D + d] = red[hh * (D + 1) + d];
     }
     __syncthreads();  // red is reused by the next combine
   };
@@ -827,7 +837,7 @@ void launch_anchor_mean_sums(const uint16_t* k, int B, int F, int T, int H, doub
   const int mt = compress_mean_tokens(B, T, H);
   const dim3 grid((T + mt - 1) / mt, B);
   constexpr int W = NT / kWave;
-  const size_t lds = (size_t)H * D * sizeof(double) +
+  const size_t lds = anchor_stage_offset(H, D) +
                      W * (q4 ? SliceStage<D / 32, true>::BYTES : SliceStage<D / 32, false>::BYTES);
   if (q4)
     hipLaunchKernelGGL((compress_anchor_mean_kernel<D, true, NT, SUMS>), grid, dim3(NT), lds, s,
@@ -917,7 +927,7 @@ size_t compress_anchor_lds_bytes(int H, int D, bool q4) {
   const int W = mean_block_threads(H) / kWave;
   const size_t stage = D == 128 ? (q4 ? SliceStage<4, true>::BYTES : SliceStage<4, false>::BYTES)
                                 : (q4 ? SliceStage<2, true>::BYTES : SliceStage<2, false>::BYTES);
-  return (size_t)H * D * sizeof(double) + W * stage;
+  return anchor_stage_offset(H, D) + W * stage;
 }
 
 size_t compress_score_lds_bytes(int B, int F, int T, int H, int D, bool mean, bool q4) {
