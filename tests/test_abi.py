@@ -60,6 +60,19 @@ def test_abi_version_and_keep_count(w):
     assert w.wkv_attention_workspace_bytes(0, 1, 1, 128) == 0
 
 
+def test_attention_split_plan(w):
+    """Without a GPU the planner assumes 256 CUs, two blocks each: 512 slots.
+    A grid just past a whole number of rounds is split in two; the 14B-class
+    shape (1480 blocks, its last round 456 of 512) and a last round over 3/8
+    full are not."""
+    per_row = 128 * 4 + 8          # float32 partial row + (max, sum) per split
+    assert w.wkv_attention_workspace_bytes(4680, 32760, 40, 128) == 0
+    assert w.wkv_attention_workspace_bytes(13 * 128, 32760, 40, 128) == 2 * 40 * 13 * 128 * per_row
+    assert w.wkv_attention_workspace_bytes(26 * 128, 32760, 40, 128) == 2 * 40 * 26 * 128 * per_row
+    assert w.wkv_attention_workspace_bytes(18 * 128, 32760, 40, 128) == 0   # 0.41 of a round left
+    assert w.wkv_attention_workspace_bytes(13 * 128, 960, 40, 128) == 0     # 15 key tiles: splits need 8 each
+
+
 def test_keep_count_matches_oracle(w):
     from oracle import wkv_oracle as O
     for F in (2, 3, 4):

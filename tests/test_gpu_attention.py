@@ -140,6 +140,16 @@ def test_14b_alt_ratio_full_size_sampled(w):
     attn_case(w, Nq, Nk, H, D, "14B r=0.5", sample=sample)
 
 
+def test_split_past_a_round(w):
+    # 13 query tiles x 40 heads = 520 blocks, just past one round of 512
+    # resident blocks: the planner splits the key range in two
+    Nq, Nk, H, D = 13 * 128, 4096, 40, 128
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert w.wkv_attention_workspace_bytes(Nq, Nk, H, D) > 0
+    sample = list(range(0, 32)) + list(range(Nq - 32, Nq))
+    attn_case(w, Nq, Nk, H, D, "split past a round", sample=sample)
+
+
 def test_deterministic(w):
     q, k, v = qkv(25, 2640, 15840, 12, 128)
     say("attention", "determinism")
