@@ -154,3 +154,24 @@ def test_unbatched_call(w):
     torch.cuda.synchronize()
     om = O.mean_rows(np_bits(K[0]), rows=ki.cpu().numpy())
     assert float(np.max(np.abs(km.cpu().numpy() - om))) <= KM_ABS
+
+
+def test_nan_and_zero_keys(w):
+    # A NaN in a kept key row reaches exactly its (head, dim) of the mean, as
+    # in the oracle; all-zero keys give a zero mean.
+    F, T, H, D = 3, 64, 2, 64
+    K, V = gen_units(40, 2, F, T, H, D)
+    K = K.clone()
+    K[0, 5, 1, 7] = float("nan")        # an anchor row: always kept
+    K[1] = 0
+    say("compress key mean", "NaN and zero keys")
+    km = torch.empty((2, H, D), dtype=torch.float64, device=DEV)
+    _, _, ki, _ = w.wkv_compress_chunk(K.to(DEV), V.to(DEV), F, T, 0.5, key_mean=km)
+    torch.cuda.synchronize()
+    g = km.cpu().numpy()
+    om = O.mean_rows(np_bits(K[0]), rows=ki[0].cpu().numpy())
+    assert np.array_equal(np.isnan(g[0]), np.isnan(om))
+    assert np.isnan(g[0, 1, 7]) and np.sum(np.isnan(g[0])) == 1
+    ok = ~np.isnan(om)
+    assert float(np.max(np.abs(g[0][ok] - om[ok]))) <= KM_ABS
+    assert np.all(g[1] == 0.0)
