@@ -161,7 +161,7 @@ def algorithmic_bytes(c, Lc, n_keep, Nk):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {a.gpus} is not "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {a.gpus} is not "
               "supported (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
